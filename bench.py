@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused OPD loss forward + backward + verify path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train]
+
+A step is one call of opd_fused_fwd_bwd_verify over the whole workload (every row: loss, both
+top-1s, row statistics, dz, then the accept length of every block), with inputs already resident in
+HBM. Prints one JSON line:
+
+* value / unit: rows per second of the whole step (host clock around K steps, bracketed by
+  torch.cuda.synchronize()).
+* roofline: the row-team kernel (the only kernel that touches the logits) timed with HIP events on
+  its stream over K launches without verification; achieved = algorithmic bytes per launch
+  (read z and y once, write dz once, plus 44 bytes of per-row outputs) / average launch time,
+  against the MI355X HBM peak of 8 TB/s. traffic = HBM bytes per launch from the rocprofv3
+  FETCH_SIZE / WRITE_SIZE counters recorded in profiles/ for the current kernel source (null if the
+  kernel changed since they were taken).
+* cpu_baseline: the float64 oracle (loss, gradient, top-1s, accept lengths) on a bounded sample of
+  the same workload, on the host cores, timed on rank 0 before the GPU is touched.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+ROW_OUTPUT_BYTES = 4 + 4 + 4 + 32  # loss, two top-1s, eight row statistics
+
+WORKLOAD_TEXT = {
+    "train": "training step: 8 sequences x 2048 positions = 16384 rows (1024 blocks of 16), V=151936 bf16 "
+             "logits, dz written bf16, y at 4x (low-temperature) scale, alpha 0.7, tau 0.02",
+    "conc128": "serving verify+loss at concurrency 128: 2048 rows (128 blocks of 16), V=151936 bf16, "
+               "per-block noise, L ~ U{2..16}, alpha 0.5, tau 0.05",
+    "packed": "packed ragged batch: 128 requests, L ~ U{1..16} rows each, V=151936 bf16, peaked/flat rows",
+    "decode1": "concurrency-1 decode: 16 rows (1 block), V=151936 bf16",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("opd_kernels.hip", "opd_internal.h"):
+        with open(os.path.join(ROOT, "draft_model_distillation_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on the current kernel."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+
+_SAMPLE = {}
+
+
+def _oracle_rows(idx_range):
+    from oracle import opd_oracle as O
+
+    z, y, alpha, tau = _SAMPLE["z"], _SAMPLE["y"], _SAMPLE["alpha"], _SAMPLE["tau"]
+    out = []
+    for i in range(*idx_range):
+        dz, info = O.row_grad(z[i], y[i], alpha, tau)
+        out.append((info["loss"], info["target_top1"], info["draft_top1"]))
+    return out
+
+
+def cpu_baseline(wl, n_blocks_sample: int):
+    """Oracle on the first n_blocks_sample blocks of the workload; returns the cpu_baseline dict."""
+    import multiprocessing as mp
+
+    from oracle import opd_oracle as O
+
+    nb = min(n_blocks_sample, len(wl.lengths))
+    rows = int(wl.offsets[nb])
+    z, y = wl.rows_f64(range(rows))
+    _SAMPLE.update(z=z, y=y, alpha=wl.recipe.alpha, tau=wl.recipe.tau)
+    cores = synth.default_workers()
+    step = max(1, rows // (cores * 4))
+    chunks = [(r, min(rows, r + step)) for r in range(0, rows, step)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        t0 = time.perf_counter()
+        res = [x for part in pool.map(_oracle_rows, chunks) for x in part]
+        d = np.array([r[2] for r in res])
+        a = np.array([r[1] for r in res])
+        O.accept_lengths(d, a, wl.offsets[: nb + 1], wl.lengths[:nb])
+        dt = time.perf_counter() - t0
+    _SAMPLE.clear()
+    return {
+        "value": rows / dt,
+        "unit": "rows/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"first {nb} blocks = {rows} rows of the workload (float64 loss, dz, top-1s, accept lengths), "
+                  f"{dt:.1f} s wall on {cores} host processes",
+    }
+
+
+# ------------------------------------------------------------------ GPU
+
+
+def to_device(arr, dtype_name):
+    import torch
+
+    if dtype_name == "bf16":
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(arr)
+    return t.pin_memory().cuda(non_blocking=False) if arr.nbytes < (1 << 30) else t.cuda()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--cpu-blocks", type=int, default=512, help="blocks of the workload timed on the oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (rows shard across GPUs "
+              "without communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    t_gen = time.perf_counter()
+    wl = synth.make(args.workload)
+    rec = wl.recipe
+    print(f"[bench] generated {args.workload}: {wl.n_rows} rows x {wl.vocab} in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_blocks)
+        print(f"[bench] cpu baseline: {cpu['value']:.1f} rows/s on {cpu['cores']} cores", file=sys.stderr, flush=True)
+
+    import torch
+
+    import draft_model_distillation_amd as opd
+
+    opd.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    z = to_device(wl.z, rec.dtype)[:, : rec.vocab]
+    y = to_device(wl.y, rec.dtype)[:, : rec.vocab]
+    off = torch.from_numpy(wl.offsets).to(dev)
+    lens = torch.from_numpy(wl.lengths).to(dev)
+    dz_dtype = torch.bfloat16 if rec.dz_dtype == "bf16" else torch.float32
+    n = wl.n_rows
+    out = {
+        "loss": torch.empty(n, dtype=torch.float32, device=dev),
+        "target_top1": torch.empty(n, dtype=torch.int32, device=dev),
+        "draft_top1": torch.empty(n, dtype=torch.int32, device=dev),
+        "row_stats": torch.empty(n, 8, dtype=torch.float32, device=dev),
+        "dz": torch.empty(n, rec.vocab, dtype=dz_dtype, device=dev),
+        "accept_len": torch.empty(len(wl.lengths), dtype=torch.int32, device=dev),
+    }
+    ws = opd.workspace(dev)
+    del wl
+    stream = torch.cuda.current_stream(dev)
+
+    def step(blocks=True):
+        opd.opd_fused_fwd_bwd_verify(z, y, off if blocks else None, lens if blocks else None, rec.alpha, rec.tau,
+                                     out=out, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if opd.read_flags(ws, clear=True) != 0:
+        print("[bench] device flags raised during warmup", file=sys.stderr)
+        sys.exit(1)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # dominant kernel alone: HIP events on the stream it is launched on
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step(blocks=False)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    if opd.read_flags(ws, clear=True) != 0:
+        print("[bench] device flags raised during the timed region", file=sys.stderr)
+        sys.exit(1)
+
+    ms_per_step = wall * 1e3 / args.steps
+    rows_per_s = n / (ms_per_step * 1e-3)
+    alg_bytes = n * (3 * 2 * rec.vocab + ROW_OUTPUT_BYTES) if rec.dtype == "bf16" and dz_dtype == torch.bfloat16 \
+        else n * (rec.vocab * (2 * (4 if rec.dtype == "f32" else 2) + (2 if dz_dtype == torch.bfloat16 else 4))
+                  + ROW_OUTPUT_BYTES)
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    result = {
+        "metric": "rows/s and achieved HBM GB/s, fused OPD loss fwd+bwd+verify, V=151936 bf16",
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_TEXT[args.workload],
+            "name": args.workload,
+            "rows": n,
+            "vocab": rec.vocab,
+            "blocks": int(len(lens)),
+            "alpha": rec.alpha,
+            "tau": rec.tau,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": recorded_traffic(args.workload),
+            "kernel": "k_team (fused mode)",
+            "kernel_ms": kernel_ms,
+            "algorithmic_bytes_per_launch": alg_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,374 @@
+// C-ABI entry points of the OPD loss / gradient / verify library (declared in include/opd.h).
+//
+// Host-side responsibilities: validate every argument before any HIP call, choose the launch
+// geometry (workgroups per row, rows in flight) from the device's occupancy, hand out the unique
+// exchange flags each launch needs, and enqueue the kernels on the caller's stream.
+
+#include "opd.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "opd_internal.h"
+
+static_assert(OPD_FLAG_NEG_L == opd::kFlagNegL, "flag mismatch");
+static_assert(OPD_FLAG_BAD_OFFSETS == opd::kFlagBadOffsets, "flag mismatch");
+static_assert(OPD_FLAG_SPIN_TIMEOUT == opd::kFlagSpinTimeout, "flag mismatch");
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<uint32_t> g_flag_epoch{16};
+std::atomic<uint32_t> g_spin_limit{0};
+
+constexpr int64_t kMaxVocab = 1 << 19;  // 524,288 logits per row
+
+opd_status_t fail(opd_status_t s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+opd_status_t hip_fail(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return OPD_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_size(opd_dtype_t dt) { return dt == OPD_F32 ? 4 : 2; }
+
+bool valid_dtype(opd_dtype_t dt) { return dt == OPD_F32 || dt == OPD_BF16; }
+
+opd_status_t check_logits(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+                          int64_t ld) {
+  if (n_rows > 0 && (!z || !y)) return fail(OPD_ERR_NULL, "z and y must be non-NULL");
+  if (!valid_dtype(dt)) return fail(OPD_ERR_DTYPE, "logit dtype must be OPD_F32 or OPD_BF16");
+  if (n_rows < 0 || n_rows > INT32_MAX) return fail(OPD_ERR_SHAPE, "n_rows out of range");
+  if (vocab <= 0 || vocab > kMaxVocab) return fail(OPD_ERR_SHAPE, "vocab must be in [1, 524288]");
+  if (ld < vocab) return fail(OPD_ERR_SHAPE, "ld must be >= vocab");
+  if (!aligned16(z) || !aligned16(y)) return fail(OPD_ERR_ALIGN, "z and y must be 16-byte aligned");
+  if ((ld * (int64_t)dtype_size(dt)) % 16 != 0) return fail(OPD_ERR_ALIGN, "row pitch must be a multiple of 16 bytes");
+  return OPD_OK;
+}
+
+opd_status_t check_params(float alpha, float tau) {
+  if (std::isnan(alpha) || alpha < 0.f || alpha > 1.f) return fail(OPD_ERR_PARAM, "alpha must be in [0, 1]");
+  if (std::isnan(tau)) return fail(OPD_ERR_PARAM, "tau must not be NaN");
+  return OPD_OK;
+}
+
+opd_status_t check_ws(void* ws, size_t ws_bytes) {
+  if (!ws || ws_bytes < opd::kWorkspaceBytes) return fail(OPD_ERR_WORKSPACE, "workspace missing or too small");
+  if (!aligned16(ws)) return fail(OPD_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return OPD_OK;
+}
+
+opd_status_t check_dz(const void* dz, opd_dtype_t dz_dt, int64_t n_rows, int64_t vocab, int64_t ld_dz) {
+  if (n_rows > 0 && !dz) return fail(OPD_ERR_NULL, "dz must be non-NULL");
+  if (!valid_dtype(dz_dt)) return fail(OPD_ERR_DTYPE, "dz dtype must be OPD_F32 or OPD_BF16");
+  if (ld_dz < vocab) return fail(OPD_ERR_SHAPE, "ld_dz must be >= vocab");
+  if (!aligned16(dz)) return fail(OPD_ERR_ALIGN, "dz must be 16-byte aligned");
+  if ((ld_dz * (int64_t)dtype_size(dz_dt)) % 16 != 0) return fail(OPD_ERR_ALIGN, "dz row pitch must be a multiple of 16 bytes");
+  return OPD_OK;
+}
+
+opd_status_t check_blocks(const opd_blocks_t* blocks, bool required) {
+  if (!blocks) return required ? fail(OPD_ERR_NULL, "blocks must be non-NULL") : OPD_OK;
+  if (blocks->n_blocks < 0) return fail(OPD_ERR_SHAPE, "n_blocks must be >= 0");
+  if (blocks->n_blocks > 0 && (!blocks->offsets || !blocks->L)) return fail(OPD_ERR_NULL, "blocks arrays must be non-NULL");
+  return OPD_OK;
+}
+
+// Occupancy (workgroups per CU) of each team-kernel variant and the CU count, per device.
+struct DeviceInfo {
+  int cus = 0;
+  int occ[3][2][2][2] = {};  // mode, in_bf16, out_bf16, K index
+};
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+opd_status_t device_info(int mode, int in_bf16, int out_bf16, int kidx, int K, int* cus, int* occ) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(OPD_ERR_HIP, "device index out of range");
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (d.cus == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    d.cus = n;
+  }
+  int& o = d.occ[mode][in_bf16][out_bf16][kidx];
+  if (o == 0) {
+    int n = 0;
+    e = opd::team_occupancy(mode, in_bf16, out_bf16, K, &n);
+    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    if (n <= 0) return fail(OPD_ERR_HIP, "kernel cannot be resident");
+    o = n;
+  }
+  *cus = d.cus;
+  *occ = o;
+  return OPD_OK;
+}
+
+struct Geometry {
+  int K, G, chunk_vec, nvec, n_teams, grid, xcd_map;
+};
+
+// Split a row of nvec 16-byte vectors over G workgroups of 256 threads x K slots, and choose how
+// many rows (teams) are in flight so that the whole grid is co-resident.
+opd_status_t plan(int mode, int in_bf16, int out_bf16, int64_t n_rows, int64_t vocab, Geometry* g) {
+  const int epv = in_bf16 ? 8 : 4;
+  const int nvec = (int)((vocab + epv - 1) / epv);
+  const int K = nvec <= opd::kThreads ? 1 : 5;
+  const int kidx = K == 1 ? 0 : 1;
+  const int slots = opd::kThreads * K;
+  int G = (nvec + slots - 1) / slots;
+  int chunk = (nvec + G - 1) / G;
+  chunk = ((chunk + 7) / 8) * 8;  // chunk boundaries on 128-byte lines
+  if (chunk > slots) chunk = slots;
+  G = (nvec + chunk - 1) / chunk;
+  if (G > opd::kMaxTeamSize) return fail(OPD_ERR_SHAPE, "vocab too large for one team");
+  int cus = 0, occ = 0;
+  opd_status_t s = device_info(mode, in_bf16, out_bf16, kidx, K, &cus, &occ);
+  if (s != OPD_OK) return s;
+  int64_t capacity = (int64_t)cus * occ;
+  if (capacity > opd::kMaxGrid) capacity = opd::kMaxGrid;
+  int64_t max_teams = capacity / G;
+  if (max_teams < 1) return fail(OPD_ERR_SHAPE, "row too wide for the device");
+  int64_t teams = n_rows < max_teams ? n_rows : max_teams;
+  int xcd = 0;
+  if (G > 1 && teams >= 8) {
+    teams -= teams % 8;
+    xcd = 1;
+  }
+  g->K = K;
+  g->G = G;
+  g->chunk_vec = chunk;
+  g->nvec = nvec;
+  g->n_teams = (int)teams;
+  g->grid = (int)(teams * G);
+  g->xcd_map = xcd;
+  return OPD_OK;
+}
+
+uint32_t reserve_flags(uint32_t count) {
+  while (true) {
+    uint32_t base = g_flag_epoch.fetch_add(count);
+    // skip ranges that contain 0 (a freshly zeroed workspace holds flag 0)
+    if ((uint64_t)base + count <= 0xffffffffull && base != 0) return base;
+  }
+}
+
+uint32_t spin_limit() {
+  uint32_t v = g_spin_limit.load();
+  return v ? v : opd::kDefaultSpinLimit;
+}
+
+opd_status_t run_team(int mode, const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+                      int64_t ld, float alpha, float tau, const float* grad_loss, float* loss, int32_t* target_top1,
+                      int32_t* draft_top1, float* row_stats, void* dz, opd_dtype_t dz_dt, int64_t ld_dz, void* ws,
+                      hipStream_t stream) {
+  if (n_rows == 0) return OPD_OK;
+  const int in_bf16 = dt == OPD_BF16;
+  const int out_bf16 = (mode == opd::kFused && dz_dt == OPD_BF16) ? 1 : 0;
+  Geometry g;
+  opd_status_t s = plan(mode, in_bf16, out_bf16, n_rows, vocab, &g);
+  if (s != OPD_OK) return s;
+  opd::TeamParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.z = static_cast<const uint8_t*>(z);
+  p.y = static_cast<const uint8_t*>(y);
+  p.ld_bytes = ld * (int64_t)dtype_size(dt);
+  p.vocab = (int32_t)vocab;
+  p.nvec = g.nvec;
+  p.n_rows = (int32_t)n_rows;
+  p.G = g.G;
+  p.chunk_vec = g.chunk_vec;
+  p.n_teams = g.n_teams;
+  p.xcd_map = g.xcd_map;
+  p.alpha = alpha;
+  p.tau = tau;
+  p.grad_loss = grad_loss;
+  p.loss = loss;
+  p.target_top1 = target_top1;
+  p.draft_top1 = draft_top1;
+  p.row_stats = row_stats;
+  p.dz = static_cast<uint8_t*>(dz);
+  p.ld_dz_bytes = ld_dz * (int64_t)dtype_size(dz_dt);
+  p.units = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ws) + opd::kHeaderBytes);
+  p.flags = static_cast<uint32_t*>(ws);
+  const int64_t iters = (n_rows + g.n_teams - 1) / g.n_teams;
+  if (2 * iters + 2 > 0x7fffffff) return fail(OPD_ERR_SHAPE, "too many rows");
+  p.flag_base = reserve_flags((uint32_t)(2 * iters + 2));
+  p.spin_limit = spin_limit();
+  hipError_t e = opd::launch_team(p, mode, in_bf16, out_bf16, g.K, g.grid, stream);
+  if (e != hipSuccess) return hip_fail(e, "team kernel launch");
+  return OPD_OK;
+}
+
+opd_status_t run_accept(const opd_blocks_t* blocks, int64_t n_rows, const int32_t* draft_top1,
+                        const int32_t* target_top1, int32_t* accept_len, void* ws, hipStream_t stream) {
+  if (!blocks || blocks->n_blocks == 0) return OPD_OK;
+  opd::AcceptParams a;
+  a.draft_top1 = draft_top1;
+  a.target_top1 = target_top1;
+  a.offsets = blocks->offsets;
+  a.L = blocks->L;
+  a.n_blocks = blocks->n_blocks;
+  a.n_rows = (int32_t)n_rows;
+  a.accept_len = accept_len;
+  a.flags = static_cast<uint32_t*>(ws);
+  hipError_t e = opd::launch_accept(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "accept kernel launch");
+  return OPD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t opd_workspace_size(void) { return opd::kWorkspaceBytes; }
+
+opd_status_t opd_loss_fwd(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab, int64_t ld,
+                          float alpha, float tau, float* loss, int32_t* target_top1, int32_t* draft_top1,
+                          float* row_stats, void* ws, size_t ws_bytes, hipStream_t stream) {
+  opd_status_t s = check_logits(z, y, dt, n_rows, vocab, ld);
+  if (s != OPD_OK) return s;
+  if (n_rows > 0 && (!loss || !target_top1 || !row_stats))
+    return fail(OPD_ERR_NULL, "loss, target_top1 and row_stats must be non-NULL");
+  if ((s = check_params(alpha, tau)) != OPD_OK) return s;
+  if ((s = check_ws(ws, ws_bytes)) != OPD_OK) return s;
+  return run_team(opd::kForward, z, y, dt, n_rows, vocab, ld, alpha, tau, nullptr, loss, target_top1, draft_top1,
+                  row_stats, nullptr, OPD_F32, vocab, ws, stream);
+}
+
+opd_status_t opd_loss_bwd(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab, int64_t ld,
+                          float alpha, float tau, const float* row_stats, const int32_t* target_top1,
+                          const float* grad_loss, void* dz, opd_dtype_t dz_dt, int64_t ld_dz, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  opd_status_t s = check_logits(z, y, dt, n_rows, vocab, ld);
+  if (s != OPD_OK) return s;
+  if (n_rows > 0 && (!row_stats || !target_top1))
+    return fail(OPD_ERR_NULL, "row_stats and target_top1 must be non-NULL");
+  if ((s = check_dz(dz, dz_dt, n_rows, vocab, ld_dz)) != OPD_OK) return s;
+  if ((s = check_params(alpha, tau)) != OPD_OK) return s;
+  if ((s = check_ws(ws, ws_bytes)) != OPD_OK) return s;
+  if (n_rows == 0) return OPD_OK;
+  opd::BwdParams p;
+  p.z = static_cast<const uint8_t*>(z);
+  p.y = static_cast<const uint8_t*>(y);
+  p.ld_bytes = ld * (int64_t)dtype_size(dt);
+  p.vocab = (int32_t)vocab;
+  p.nvec = (int32_t)((vocab + (dt == OPD_BF16 ? 8 : 4) - 1) / (dt == OPD_BF16 ? 8 : 4));
+  p.n_rows = (int32_t)n_rows;
+  p.alpha = alpha;
+  p.tau = tau;
+  p.row_stats = row_stats;
+  p.target_top1 = target_top1;
+  p.grad_loss = grad_loss;
+  p.dz = static_cast<uint8_t*>(dz);
+  p.ld_dz_bytes = ld_dz * (int64_t)dtype_size(dz_dt);
+  if (n_rows > 65535) {
+    // the backward grid uses blockIdx.y for the row: launch in slabs of 65535 rows
+    for (int64_t r0 = 0; r0 < n_rows; r0 += 65535) {
+      opd::BwdParams q = p;
+      const int64_t nr = (n_rows - r0) < 65535 ? (n_rows - r0) : 65535;
+      q.z = p.z + r0 * p.ld_bytes;
+      q.y = p.y + r0 * p.ld_bytes;
+      q.dz = p.dz + r0 * p.ld_dz_bytes;
+      q.row_stats = p.row_stats + 8 * r0;
+      q.target_top1 = p.target_top1 + r0;
+      q.grad_loss = p.grad_loss ? p.grad_loss + r0 : nullptr;
+      q.n_rows = (int32_t)nr;
+      hipError_t e = opd::launch_bwd(q, dt == OPD_BF16, dz_dt == OPD_BF16, stream);
+      if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+    }
+    return OPD_OK;
+  }
+  hipError_t e = opd::launch_bwd(p, dt == OPD_BF16, dz_dt == OPD_BF16, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+  return OPD_OK;
+}
+
+opd_status_t verify_accept_len(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+                               int64_t ld, const opd_blocks_t* blocks, int32_t* target_top1, int32_t* draft_top1,
+                               int32_t* accept_len, void* ws, size_t ws_bytes, hipStream_t stream) {
+  opd_status_t s = check_logits(z, y, dt, n_rows, vocab, ld);
+  if (s != OPD_OK) return s;
+  if ((s = check_blocks(blocks, true)) != OPD_OK) return s;
+  if (n_rows > 0 && (!target_top1 || !draft_top1)) return fail(OPD_ERR_NULL, "top-1 outputs must be non-NULL");
+  if (blocks->n_blocks > 0 && !accept_len) return fail(OPD_ERR_NULL, "accept_len must be non-NULL");
+  if ((s = check_ws(ws, ws_bytes)) != OPD_OK) return s;
+  s = run_team(opd::kTop1, z, y, dt, n_rows, vocab, ld, 0.5f, 0.f, nullptr, nullptr, target_top1, draft_top1,
+               nullptr, nullptr, OPD_F32, vocab, ws, stream);
+  if (s != OPD_OK) return s;
+  return run_accept(blocks, n_rows, draft_top1, target_top1, accept_len, ws, stream);
+}
+
+opd_status_t opd_fused_fwd_bwd_verify(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+                                      int64_t ld, const opd_blocks_t* blocks, float alpha, float tau,
+                                      const float* grad_loss, float* loss, int32_t* target_top1, int32_t* draft_top1,
+                                      float* row_stats, void* dz, opd_dtype_t dz_dt, int64_t ld_dz,
+                                      int32_t* accept_len, void* ws, size_t ws_bytes, hipStream_t stream) {
+  opd_status_t s = check_logits(z, y, dt, n_rows, vocab, ld);
+  if (s != OPD_OK) return s;
+  if ((s = check_blocks(blocks, false)) != OPD_OK) return s;
+  if (n_rows > 0 && (!loss || !target_top1 || !row_stats))
+    return fail(OPD_ERR_NULL, "loss, target_top1 and row_stats must be non-NULL");
+  if (blocks && blocks->n_blocks > 0 && (!accept_len || (n_rows > 0 && !draft_top1)))
+    return fail(OPD_ERR_NULL, "draft_top1 and accept_len are required when blocks are given");
+  if ((s = check_dz(dz, dz_dt, n_rows, vocab, ld_dz)) != OPD_OK) return s;
+  if ((s = check_params(alpha, tau)) != OPD_OK) return s;
+  if ((s = check_ws(ws, ws_bytes)) != OPD_OK) return s;
+  s = run_team(opd::kFused, z, y, dt, n_rows, vocab, ld, alpha, tau, grad_loss, loss, target_top1, draft_top1,
+               row_stats, dz, dz_dt, ld_dz, ws, stream);
+  if (s != OPD_OK) return s;
+  return run_accept(blocks, n_rows, draft_top1, target_top1, accept_len, ws, stream);
+}
+
+opd_status_t opd_read_flags(void* ws, size_t ws_bytes, int clear, uint32_t* flags, hipStream_t stream) {
+  if (!flags) return fail(OPD_ERR_NULL, "flags must be non-NULL");
+  opd_status_t s = check_ws(ws, ws_bytes);
+  if (s != OPD_OK) return s;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  *flags = v;
+  if (clear) {
+    e = opd::launch_fill_u32(static_cast<uint32_t*>(ws), 0u, 1, stream);
+    if (e != hipSuccess) return hip_fail(e, "flag clear");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  }
+  return OPD_OK;
+}
+
+void opd_set_spin_limit(uint32_t spins) { g_spin_limit.store(spins); }
+
+const char* opd_status_string(opd_status_t s) {
+  switch (s) {
+    case OPD_OK: return "OPD_OK";
+    case OPD_ERR_NULL: return "OPD_ERR_NULL: a required pointer is NULL";
+    case OPD_ERR_SHAPE: return "OPD_ERR_SHAPE: invalid sizes";
+    case OPD_ERR_DTYPE: return "OPD_ERR_DTYPE: unsupported dtype";
+    case OPD_ERR_ALIGN: return "OPD_ERR_ALIGN: pointer or row pitch not 16-byte aligned";
+    case OPD_ERR_PARAM: return "OPD_ERR_PARAM: alpha or tau invalid";
+    case OPD_ERR_WORKSPACE: return "OPD_ERR_WORKSPACE: workspace missing or too small";
+    case OPD_ERR_HIP: return "OPD_ERR_HIP: HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* opd_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Internal interface between the C-ABI host layer (opd_api.cpp) and the gfx950 kernels
+// (opd_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace opd {
+
+constexpr int kThreads = 256;  // workgroup size of every row kernel (4 wave64)
+constexpr int kStage1Units = 7;
+constexpr int kStage2Units = 2;
+constexpr int kMaxGrid = 4096;  // upper bound on co-resident workgroups the workspace is sized for
+// Workspace layout: [0, 256) header (flag word at offset 0), then the exchange units.
+constexpr size_t kHeaderBytes = 256;
+constexpr size_t kUnitBytesPerWg = 2 * 8 * 8;  // two stages x up to 8 units x 8 bytes
+constexpr size_t kWorkspaceBytes = kHeaderBytes + (size_t)kMaxGrid * kUnitBytesPerWg;
+
+// Sticky device flag bits (same values as the public OPD_FLAG_* macros).
+constexpr uint32_t kFlagNegL = 1u;
+constexpr uint32_t kFlagBadOffsets = 2u;
+constexpr uint32_t kFlagSpinTimeout = 4u;
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;
+constexpr int kMaxTeamSize = 128;
+
+enum Mode : int { kFused = 0, kForward = 1, kTop1 = 2 };
+
+// One launch of the row-team kernel: G workgroups share a row, each owns a chunk of it.
+struct TeamParams {
+  const uint8_t* z;
+  const uint8_t* y;
+  int64_t ld_bytes;  // row pitch of z and y in bytes
+  int32_t vocab;
+  int32_t nvec;       // 16-byte vectors per row covering vocab
+  int32_t n_rows;
+  int32_t G;          // workgroups per row
+  int32_t chunk_vec;  // vectors per chunk (last chunk may be shorter)
+  int32_t n_teams;
+  int32_t xcd_map;    // 1: members of a team are dispatched to the same XCD
+  float alpha;
+  float tau;
+  const float* grad_loss;  // nullable
+  float* loss;
+  int32_t* target_top1;
+  int32_t* draft_top1;  // nullable
+  float* row_stats;     // [n_rows][8]; nullable in kTop1 mode
+  uint8_t* dz;
+  int64_t ld_dz_bytes;
+  uint64_t* units;  // exchange units [n_teams][2][G][8]
+  uint32_t* flags;  // sticky flag word
+  uint32_t flag_base;
+  uint32_t spin_limit;
+};
+
+struct BwdParams {
+  const uint8_t* z;
+  const uint8_t* y;
+  int64_t ld_bytes;
+  int32_t vocab;
+  int32_t nvec;
+  int32_t n_rows;
+  float alpha;
+  float tau;
+  const float* row_stats;  // [n_rows][8] from the forward pass
+  const int32_t* target_top1;
+  const float* grad_loss;
+  uint8_t* dz;
+  int64_t ld_dz_bytes;
+};
+
+struct AcceptParams {
+  const int32_t* draft_top1;
+  const int32_t* target_top1;
+  const int32_t* offsets;
+  const int32_t* L;
+  int32_t n_blocks;
+  int32_t n_rows;
+  int32_t* accept_len;
+  uint32_t* flags;
+};
+
+// in_bf16: 1 if z/y are bf16 (else fp32); out_bf16: 1 if dz is bf16 (else fp32); K: slots/thread.
+hipError_t launch_team(const TeamParams& p, int mode, int in_bf16, int out_bf16, int K, int grid,
+                       hipStream_t s);
+hipError_t team_occupancy(int mode, int in_bf16, int out_bf16, int K, int* blocks_per_cu);
+hipError_t launch_bwd(const BwdParams& p, int in_bf16, int out_bf16, hipStream_t s);
+hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, size_t count, hipStream_t s);
+
+}  // namespace opd

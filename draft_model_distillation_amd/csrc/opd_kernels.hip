@@ -1,0 +1,820 @@
+// gfx950 kernels of the on-policy-distillation (OPD) loss / gradient / greedy-verify path.
+//
+// What is computed, per drafted position (one row of V logits), follows the AdaFlash pages:
+//  - "AdaFlash: Adaptive Speculative Decoding with Online Self-Improvement for High-Concurrency LLM
+//    Inference" (besthub.dev article), section "1. On-Policy Distillation (OPD) for Domain
+//    Adaptation": reverse KL of the drafter p = softmax(z) against the target q = softmax(y), each
+//    vocabulary term clipped from above before the sum, mixed with cross entropy on the target's
+//    top-1 token; the drafter is what gets updated, so the gradient is taken with respect to z.
+//  - same article, section "2. Adaptive Length Head for Token-Level Variance": greedy acceptance of
+//    a drafted block within the predicted verification length L.
+//  - same article, section "Infrastructure: ... Variable-Length Batching": packed ragged blocks.
+//
+// Design (MI355X): the path is HBM-bound streaming (no dense contraction, so no MFMA). A 151,936-wide
+// bf16 row is 297 KiB per tensor, more than one CU can hold, so a row is split over a *team* of G
+// workgroups. Each workgroup keeps its chunk of z and y in VGPRs (packed bf16) for the whole row:
+//   phase A  chunk max, sum-exp of z and y, per-vector sums of e^(z_v - m) and e^(z_v - m)(z_v - y_v),
+//            first argmax of z and y
+//   -- exchange 1 --  every member combines the G partials in the same fixed order
+//   phase B  S and the clipped reverse KL: vectors whose bound max(p) * max(z - y - delta, 0) is
+//            <= tau provably hold no clipped term and use their phase-A sums; the rest are visited
+//            element by element
+//   -- exchange 2 --
+//   phase C  dz written once (bf16 rounded to nearest even, or fp32)
+// so z and y are read from HBM once and dz written once. Exchanges use 8-byte [value | flag] units
+// written and polled with agent-scope relaxed atomics (sc1: coherent across XCDs without L2
+// writeback / invalidate); the flag is unique per launch, row iteration and stage, so nothing has to
+// be reset between launches and a stale unit can never be taken for a fresh one. Every wait is
+// bounded and raises a sticky flag instead of hanging. Team members are mapped to one XCD when the
+// team count allows (workgroups are dispatched round-robin over the 8 XCDs).
+//
+// Numerics: fp32 throughout with fixed reduction orders (bitwise deterministic). Per row, with
+// M = max z, S_z = sum_v e^(z_v - M), delta = LSE(z) - LSE(y), t_v = p_v (z_v - y_v - delta):
+//   clipped reverse KL = sum_v min(t_v, tau),  S = sum_v [t_v <= tau] p_v (t_v / p_v + 1),
+//   dz_v = w p_v (alpha (z_v - y_v) + alpha (1 - delta - S) + 1 - alpha)  (unclipped)
+//   dz_v = w p_v (1 - alpha - alpha S)                                     (clipped)
+//   dz_a -= w (1 - alpha).
+// p_v is evaluated from M and log S_z held apart (RowConst), so that large logits keep full fp32
+// relative accuracy. Vectors proven free of clipped terms contribute to S and the reverse KL
+// through their per-vector sums from phase A; vectors near the peak are summed element by element
+// (no cancellation between the clipped terms and the rest). The clip decision is the same fp32
+// test, from the same per-row floats, in the fused and the separate kernels, so fused and
+// forward+backward results are bit-identical.
+
+#include <stdint.h>
+
+#include "opd_internal.h"
+
+namespace opd {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kBig = 0x7fffffff;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- input formats (16-byte vectors)
+
+struct F32In {
+  static constexpr int EPV = 4;
+  // -9.95e29: contributes 0 to every sum and never wins a max (inputs satisfy |logit| <= 1e4)
+  static constexpr uint32_t kSentinel = 0xF1490000u;
+  __device__ static __forceinline__ void decode(const uint4& v, float (&x)[EPV]) {
+    x[0] = __uint_as_float(v.x);
+    x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z);
+    x[3] = __uint_as_float(v.w);
+  }
+  __device__ static __forceinline__ uint32_t tail_word(uint32_t w, int j, int nvalid) {
+    return j < nvalid ? w : kSentinel;
+  }
+};
+
+struct BF16In {
+  static constexpr int EPV = 8;
+  static constexpr uint32_t kSentinel = 0xF149F149u;
+  __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static __forceinline__ void decode(const uint4& v, float (&x)[EPV]) {
+    x[0] = lo(v.x);
+    x[1] = hi(v.x);
+    x[2] = lo(v.y);
+    x[3] = hi(v.y);
+    x[4] = lo(v.z);
+    x[5] = hi(v.z);
+    x[6] = lo(v.w);
+    x[7] = hi(v.w);
+  }
+  __device__ static __forceinline__ uint32_t tail_word(uint32_t w, int j, int nvalid) {
+    if (2 * j >= nvalid) return kSentinel;
+    if (2 * j + 1 >= nvalid) return (w & 0xffffu) | (kSentinel & 0xffff0000u);
+    return w;
+  }
+};
+
+template <class In>
+__device__ __forceinline__ void mask_tail(uint4& v, int nvalid) {
+  v.x = In::tail_word(v.x, 0, nvalid);
+  v.y = In::tail_word(v.y, 1, nvalid);
+  v.z = In::tail_word(v.z, 2, nvalid);
+  v.w = In::tail_word(v.w, 3, nvalid);
+}
+
+__device__ __forceinline__ uint4 splat4(uint32_t s) { return make_uint4(s, s, s, s); }
+
+// ---------------------------------------------------------------- output formats
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));  // v_cvt_pk_bf16_f32, RNE
+}
+
+template <bool OutBF16, int EPV>
+__device__ __forceinline__ void store_vec(uint8_t* dst, const float (&o)[EPV]) {
+  if constexpr (OutBF16) {
+    if constexpr (EPV == 8) {
+      *(uint4*)dst = make_uint4(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
+                                pack_bf16(o[6], o[7]));
+    } else {
+      *(uint2*)dst = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < EPV / 4; ++q) {
+      *(float4*)(dst + 16 * q) = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    }
+  }
+}
+
+template <bool OutBF16, int EPV>
+__device__ __forceinline__ void store_partial(uint8_t* dst, const float (&o)[EPV], int nvalid) {
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) {
+    if (e < nvalid) {
+      if constexpr (OutBF16) {
+        uint32_t pk = pack_bf16(o[e], 0.f);
+        *(uint16_t*)(dst + 2 * e) = (uint16_t)(pk & 0xffffu);
+      } else {
+        *(float*)(dst + 4 * e) = o[e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- wave / block reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+// (index, value) pair: smaller index wins
+__device__ __forceinline__ void wave_min_pair(int& i, float& v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    int oi = __shfl_xor(i, o);
+    float ov = __shfl_xor(v, o);
+    if (oi < i) {
+      i = oi;
+      v = ov;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- cross-workgroup exchange
+
+__device__ __forceinline__ void unit_store(uint64_t* p, uint32_t flag, uint32_t bits) {
+  uint64_t u = ((uint64_t)flag << 32) | (uint64_t)bits;
+  __hip_atomic_store(p, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll one unit until its flag matches; returns false when the bound was exceeded.
+__device__ __forceinline__ bool unit_wait(const uint64_t* p, uint32_t flag, uint32_t limit, uint32_t& bits) {
+  uint32_t spins = 0;
+  while (true) {
+    uint64_t u = __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(u >> 32) == flag) {
+      bits = (uint32_t)u;
+      return true;
+    }
+    if (++spins > limit) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+struct Shared {
+  float red[4][8];
+  int ired[4][4];
+  float out[8];
+  uint32_t rx[128 * kStage1Units];
+  int err;
+};
+
+// Publish NU values of this chunk and gather every chunk's values into sh.rx[c * NU + j].
+// Returns false (uniformly over the workgroup) if a wait exceeded its bound.
+template <int NU>
+__device__ __forceinline__ bool exchange(Shared& sh, const TeamParams& P, int team, int chunk, int stage,
+                                         uint32_t flag, bool receive) {
+  uint64_t* base = P.units + ((size_t)team * 2 + stage) * (size_t)P.G * 8;
+  const int tid = threadIdx.x;
+  if (tid < NU) {
+    unit_store(base + (size_t)chunk * 8 + tid, flag, __float_as_uint(sh.out[tid]));
+  }
+  if (receive) {
+    bool ok = true;
+    for (int i = tid; i < P.G * NU; i += kThreads) {
+      uint32_t bits = 0;
+      const int c = i / NU, j = i - c * NU;
+      if (!unit_wait(base + (size_t)c * 8 + j, flag, P.spin_limit, bits)) ok = false;
+      sh.rx[i] = bits;
+    }
+    if (!ok) sh.err = 1;
+  }
+  __syncthreads();
+  return sh.err == 0;
+}
+
+// ---------------------------------------------------------------- per-row constants
+
+// Probability of a logit x under the row's softmax, p(x) = exp(x - LSE(z)), evaluated as
+// exp2(fma(x, log2 e, -c_hi) - c_lo) with c_hi + c_lo = M_z log2 e + log2 S_z carried in two floats:
+// fma forms x log2 e - c_hi with a single rounding, so p keeps full fp32 relative accuracy even for
+// logits in the thousands (a single fp32 constant LSE log2 e would be off by up to half an ulp of
+// ~1.4e4, i.e. 1e-3 in p). The same function, from the same stored floats, is used by the fused
+// kernel and by the separate backward kernel, so their clip decisions agree bit for bit.
+struct RowConst {
+  float c_hi, c_lo;  // p(x) = exp2(fma(x, log2e, -c_hi) - c_lo)
+  float delta;       // LSE(z) - LSE(y)
+  __device__ __forceinline__ void init(float m_z, float ln_sz, float d) {
+    c_hi = m_z * kLog2e;
+    c_lo = __builtin_fmaf(m_z, kLog2e, -c_hi) + ln_sz * kLog2e;
+    delta = d;
+  }
+  __device__ __forceinline__ float p(float x) const {
+    return exp2_fast(__builtin_fmaf(x, kLog2e, -c_hi) - c_lo);
+  }
+};
+
+// Keeps the packed inputs opaque between phases so that the compiler re-decodes them (1 VALU op per
+// element) instead of keeping decoded fp32 copies alive across the exchanges (which doubles the VGPR
+// footprint and halves occupancy).
+__device__ __forceinline__ void opaque(uint4& v) {
+  __asm__ volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+// Ends a slot: the slot's results must exist here, so the scheduler cannot interleave all K slots
+// (which keeps every slot's decoded inputs and exponentials live at once).
+__device__ __forceinline__ void fence_vals(float& a) { __asm__ volatile("" : "+v"(a)); }
+__device__ __forceinline__ void fence_vals(float& a, float& b) { __asm__ volatile("" : "+v"(a), "+v"(b)); }
+__device__ __forceinline__ void fence_vals(float& a, float& b, float& c, float& d) {
+  __asm__ volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+// ---------------------------------------------------------------- the row-team kernel
+
+template <class In, bool OutBF16, int K, int MODE>
+__global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
+  constexpr int EPV = In::EPV;
+  constexpr int OSZ = OutBF16 ? 2 : 4;
+  __shared__ Shared sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int b = blockIdx.x;
+  int team, chunk;
+  if (P.xcd_map) {
+    const int x = b & 7, local = b >> 3;
+    team = (local / P.G) * 8 + x;
+    chunk = local % P.G;
+  } else {
+    team = b / P.G;
+    chunk = b % P.G;
+  }
+  const int cv0 = chunk * P.chunk_vec;
+  const int cv1 = min(cv0 + P.chunk_vec, P.nvec);
+  const float alpha = P.alpha, tau = P.tau;
+  const bool tail_chunk = (cv1 == P.nvec) && (P.nvec * EPV != P.vocab);
+  if (tid == 0) sh.err = 0;
+
+  int iter = 0;
+  for (int row = team; row < P.n_rows; row += P.n_teams, ++iter) {
+    __syncthreads();
+    // Per-thread vector index, made opaque each row: otherwise the compiler hoists every element's
+    // index and bounds test out of the row loop and keeps them all in registers.
+    int tv = cv0 + tid;
+    __asm__ volatile("" : "+v"(tv));
+    const uint4* zrow = (const uint4*)(P.z + (int64_t)row * P.ld_bytes);
+    const uint4* yrow = (const uint4*)(P.y + (int64_t)row * P.ld_bytes);
+    // All K loads of z and y are issued back to back (indices clamped into the chunk, so no branch
+    // and no wait between them); slots past the chunk end are replaced by the sentinel afterwards.
+    uint4 zr[K], yr[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int vc = min(tv + k * kThreads, cv1 - 1);
+      zr[k] = zrow[vc];
+      yr[k] = yrow[vc];
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {  // pins the loads here (else they are sunk into branches)
+      opaque(zr[k]);
+      opaque(yr[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const bool in = tv + k * kThreads < cv1;
+      zr[k] = in ? zr[k] : splat4(In::kSentinel);
+      yr[k] = in ? yr[k] : splat4(In::kSentinel);
+    }
+    if (tail_chunk) {  // wave-uniform: only the chunk holding a partial last vector
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int vi = tv + k * kThreads;
+        if (vi == P.nvec - 1) {
+          mask_tail<In>(zr[k], P.vocab - vi * EPV);
+          mask_tail<In>(yr[k], P.vocab - vi * EPV);
+        }
+      }
+    }
+
+    // ---- phase A1: maxima (per vector of z, per lane of y)
+    float zmv[K];
+    float lzmax = kNegInf, lymax = kNegInf;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      float x[EPV], w[EPV];
+      In::decode(zr[k], x);
+      In::decode(yr[k], w);
+      float a = x[0], c = w[0];
+#pragma unroll
+      for (int e = 1; e < EPV; ++e) {
+        a = fmaxf(a, x[e]);
+        c = fmaxf(c, w[e]);
+      }
+      zmv[k] = a;
+      lzmax = fmaxf(lzmax, a);
+      lymax = fmaxf(lymax, c);
+      fence_vals(lzmax, lymax);
+    }
+    {
+      const float a = wave_max(lzmax), c = wave_max(lymax);
+      if (lane == 0) {
+        sh.red[wave][0] = a;
+        sh.red[wave][1] = c;
+      }
+    }
+    __syncthreads();
+    const float m_z = fmaxf(fmaxf(sh.red[0][0], sh.red[1][0]), fmaxf(sh.red[2][0], sh.red[3][0]));
+    const float m_y = fmaxf(fmaxf(sh.red[0][1], sh.red[1][1]), fmaxf(sh.red[2][1], sh.red[3][1]));
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      opaque(zr[k]);
+      opaque(yr[k]);
+    }
+
+    // ---- lowest index of each chunk maximum: only lanes holding it scan, from the top down with
+    // selects, so the last hit is the lowest index
+    int iz = kBig, iy = kBig;
+    float zat = 0.f;
+    if (lzmax == m_z) {
+      int code = 0;
+#pragma unroll
+      for (int k = K - 1; k >= 0; --k) {
+        float x[EPV];
+        In::decode(zr[k], x);
+#pragma unroll
+        for (int e = EPV - 1; e >= 0; --e) code = (x[e] == m_z) ? k * EPV + e : code;
+      }
+      iz = (tv + (code / EPV) * kThreads) * EPV + code % EPV;
+    }
+    if (lymax == m_y) {
+      int code = 0;
+#pragma unroll
+      for (int k = K - 1; k >= 0; --k) {
+        float x[EPV], w[EPV];
+        In::decode(zr[k], x);
+        In::decode(yr[k], w);
+#pragma unroll
+        for (int e = EPV - 1; e >= 0; --e) {
+          const bool hit = (w[e] == m_y);
+          code = hit ? k * EPV + e : code;
+          zat = hit ? x[e] : zat;
+        }
+      }
+      iy = (tv + (code / EPV) * kThreads) * EPV + code % EPV;
+    }
+
+    // ---- phase A2: exponential sums relative to the chunk maxima. E_k, B_k per vector are kept:
+    // phase B turns them into the unclipped part of S and of the reverse KL without cancellation.
+    float dmv[K], ek[K], bk[K];
+    float sy = 0.f;
+    float cz_hi = 0.f, cz_lo = 0.f, cy_lo = 0.f;
+    if constexpr (MODE != kTop1) {
+      cz_hi = m_z * kLog2e;
+      cz_lo = __builtin_fmaf(m_z, kLog2e, -cz_hi);
+      const float cy_hi = m_y * kLog2e;
+      cy_lo = __builtin_fmaf(m_y, kLog2e, -cy_hi);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        opaque(zr[k]);
+        opaque(yr[k]);
+        float x[EPV], w[EPV];
+        In::decode(zr[k], x);
+        In::decode(yr[k], w);
+        float dm = kNegInf, se = 0.f, sb = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float d = x[e] - w[e];
+          dm = fmaxf(dm, d);
+          const float ez = exp2_fast(__builtin_fmaf(x[e], kLog2e, -cz_hi));
+          se += ez;
+          sb = __builtin_fmaf(ez, d, sb);
+          sy += exp2_fast(__builtin_fmaf(w[e], kLog2e, -cy_hi));
+        }
+        fence_vals(dm, se, sb, sy);
+        dmv[k] = dm;
+        ek[k] = se;
+        bk[k] = sb;
+      }
+    }
+    float sz = 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) sz += (MODE != kTop1) ? ek[k] : 0.f;
+    {
+      sz = wave_sum(sz);
+      sy = wave_sum(sy);
+      iz = wave_min(iz);
+      wave_min_pair(iy, zat);
+      if (lane == 0) {
+        sh.red[wave][2] = sz;
+        sh.red[wave][3] = sy;
+        sh.red[wave][5] = zat;
+        sh.ired[wave][0] = iz;
+        sh.ired[wave][1] = iy;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float tsz = (sh.red[0][2] + sh.red[1][2]) + (sh.red[2][2] + sh.red[3][2]);
+      float tsy = (sh.red[0][3] + sh.red[1][3]) + (sh.red[2][3] + sh.red[3][3]);
+      float tz = 0.f;
+      int tiz = kBig, tiy = kBig;
+      for (int q = 0; q < 4; ++q) {
+        tiz = min(tiz, sh.ired[q][0]);
+        if (sh.ired[q][1] < tiy) {
+          tiy = sh.ired[q][1];
+          tz = sh.red[q][5];
+        }
+      }
+      // undo the rounding of the exponent offsets: sums become sum_v e^(x_v - m) exactly scaled
+      sh.out[0] = m_z;
+      sh.out[1] = tsz * exp2_fast(-cz_lo);
+      sh.out[2] = m_y;
+      sh.out[3] = tsy * exp2_fast(-cy_lo);
+      sh.out[4] = __int_as_float(tiz);
+      sh.out[5] = __int_as_float(tiy);
+      sh.out[6] = tz;
+    }
+    __syncthreads();
+
+    const uint32_t flag1 = P.flag_base + 2u * (uint32_t)iter;
+    if (P.G > 1) {
+      if (!exchange<kStage1Units>(sh, P, team, chunk, 0, flag1, true)) break;
+    }
+
+    // ---- combine the G chunk partials in chunk order (identical in every member)
+    float Mz = kNegInf, My = kNegInf;
+    float Sz = 0.f, Sy = 0.f, za = 0.f;
+    int dtop = kBig, atop = kBig;
+    if (P.G > 1) {
+      for (int c = 0; c < P.G; ++c) {
+        Mz = fmaxf(Mz, __uint_as_float(sh.rx[c * kStage1Units + 0]));
+        My = fmaxf(My, __uint_as_float(sh.rx[c * kStage1Units + 2]));
+      }
+      for (int c = 0; c < P.G; ++c) {
+        const uint32_t* u = sh.rx + c * kStage1Units;
+        const float mzc = __uint_as_float(u[0]), myc = __uint_as_float(u[2]);
+        if constexpr (MODE != kTop1) {
+          Sz = __builtin_fmaf(__uint_as_float(u[1]), exp2_fast((mzc - Mz) * kLog2e), Sz);
+          Sy = __builtin_fmaf(__uint_as_float(u[3]), exp2_fast((myc - My) * kLog2e), Sy);
+        }
+        if (dtop == kBig && mzc == Mz) dtop = (int)u[4];
+        if (atop == kBig && myc == My) {
+          atop = (int)u[5];
+          za = __uint_as_float(u[6]);
+        }
+      }
+    } else {
+      Mz = sh.out[0];
+      Sz = sh.out[1];
+      My = sh.out[2];
+      Sy = sh.out[3];
+      dtop = __float_as_int(sh.out[4]);
+      atop = __float_as_int(sh.out[5]);
+      za = sh.out[6];
+    }
+
+    if constexpr (MODE == kTop1) {
+      if (chunk == 0 && tid == 0) {
+        P.target_top1[row] = atop;
+        P.draft_top1[row] = dtop;
+      }
+      continue;
+    } else {
+      const float ln_sz = logf(Sz);
+      const float ln_sy = logf(Sy);
+      RowConst rc;
+      rc.init(Mz, ln_sz, (Mz - My) + (ln_sz - ln_sy));
+      const float delta = rc.delta;
+
+      // ---- phase B. Vector bound: every t_v of a vector is <= p(max z) * max(max(z - y) - delta, 0)
+      // (same monotone p() and subtraction as the element test), so a vector whose bound is <= tau
+      // holds no clipped term and its S / reverse-KL contributions come from E_k, B_k. Vectors near
+      // the peak are summed element by element.
+      const float scale = exp2_fast((cz_hi - rc.c_hi) - rc.c_lo);  // e-units of this chunk -> p
+      const float one_m_delta = 1.f - delta;
+      float s_fast = 0.f, r_fast = 0.f, s_slow = 0.f, r_slow = 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float ub = rc.p(zmv[k]) * fmaxf(dmv[k] - delta, 0.f);
+        if (ub <= tau) {
+          s_fast += __builtin_fmaf(one_m_delta, ek[k], bk[k]);
+          r_fast += __builtin_fmaf(-delta, ek[k], bk[k]);
+        } else {
+          opaque(zr[k]);
+          opaque(yr[k]);
+          float x[EPV], w[EPV];
+          In::decode(zr[k], x);
+          In::decode(yr[k], w);
+          const int vi = tv + k * kThreads;
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const bool valid = (vi < cv1) && (vi * EPV + e < P.vocab);
+            const float p = rc.p(x[e]);
+            const float t = p * ((x[e] - w[e]) - delta);
+            const bool clipped = t > tau;
+            r_slow += valid ? (clipped ? tau : t) : 0.f;
+            s_slow += (valid && !clipped) ? (t + p) : 0.f;
+          }
+          fence_vals(r_slow, s_slow);
+        }
+      }
+      float s_c = __builtin_fmaf(scale, s_fast, s_slow);
+      float r_c = __builtin_fmaf(scale, r_fast, r_slow);
+      s_c = wave_sum(s_c);
+      r_c = wave_sum(r_c);
+      if (lane == 0) {
+        sh.red[wave][6] = s_c;
+        sh.red[wave][7] = r_c;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        sh.out[0] = (sh.red[0][6] + sh.red[1][6]) + (sh.red[2][6] + sh.red[3][6]);
+        sh.out[1] = (sh.red[0][7] + sh.red[1][7]) + (sh.red[2][7] + sh.red[3][7]);
+      }
+      __syncthreads();
+      float S = 0.f, rkl = 0.f;
+      const bool need_rx2 = (MODE == kFused) || chunk == 0;
+      if (P.G > 1) {
+        if (!exchange<kStage2Units>(sh, P, team, chunk, 1, flag1 + 1u, need_rx2)) break;
+        if (need_rx2) {
+          for (int c = 0; c < P.G; ++c) {
+            S += __uint_as_float(sh.rx[c * kStage2Units + 0]);
+            rkl += __uint_as_float(sh.rx[c * kStage2Units + 1]);
+          }
+        }
+      } else {
+        S = sh.out[0];
+        rkl = sh.out[1];
+      }
+      if (chunk == 0 && tid == 0) {
+        const float ce = (Mz - za) + ln_sz;
+        float* st = P.row_stats + 8 * (int64_t)row;
+        P.loss[row] = alpha * rkl + (1.f - alpha) * ce;
+        P.target_top1[row] = atop;
+        if (P.draft_top1) P.draft_top1[row] = dtop;
+        st[0] = Mz + ln_sz;
+        st[1] = My + ln_sy;
+        st[2] = S;
+        st[3] = rkl;
+        st[4] = Mz;
+        st[5] = ln_sz;
+        st[6] = delta;
+        st[7] = ce;
+      }
+
+      if constexpr (MODE == kFused) {
+        // ---- phase C: dz (coefficients shared with k_bwd)
+        const float wrow = P.grad_loss ? P.grad_loss[row] : 1.f;
+        const float wa = wrow * alpha;
+        const float k0 = wrow * (alpha * (one_m_delta - S) + (1.f - alpha));
+        const float kc = wrow * ((1.f - alpha) - alpha * S);
+        const float wce = wrow * (1.f - alpha);
+        uint8_t* drow = P.dz + (int64_t)row * P.ld_dz_bytes;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int vi = tv + k * kThreads;
+          if (vi < cv1) {
+            opaque(zr[k]);
+            opaque(yr[k]);
+            float x[EPV], w[EPV], o[EPV];
+            In::decode(zr[k], x);
+            In::decode(yr[k], w);
+            const bool slow = rc.p(zmv[k]) * fmaxf(dmv[k] - delta, 0.f) > tau;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+              const float p = rc.p(x[e]);
+              const float d = x[e] - w[e];
+              float coef = __builtin_fmaf(wa, d, k0);
+              if (slow) coef = (p * (d - delta) > tau) ? kc : coef;
+              o[e] = p * coef;
+            }
+            const int g0 = vi * EPV;
+            if (atop >= g0 && atop < g0 + EPV) {
+#pragma unroll
+              for (int e = 0; e < EPV; ++e) o[e] = (g0 + e == atop) ? o[e] - wce : o[e];
+            }
+            uint8_t* dst = drow + (int64_t)g0 * OSZ;
+#pragma unroll
+            for (int e = 0; e < EPV; e += 4) fence_vals(o[e], o[e + 1], o[e + 2], o[e + 3]);
+            if (g0 + EPV <= P.vocab) {
+              store_vec<OutBF16, EPV>(dst, o);
+            } else {
+              store_partial<OutBF16, EPV>(dst, o, P.vocab - g0);
+            }
+          }
+        }
+      }
+    }
+  }
+  if (sh.err && tid == 0) atomicOr(P.flags, (uint32_t)kFlagSpinTimeout);
+}
+
+// ---------------------------------------------------------------- streaming backward
+
+constexpr int kBwdVecPerThread = 4;
+
+template <class In, bool OutBF16>
+__global__ void __launch_bounds__(kThreads) k_bwd(BwdParams P) {
+  constexpr int EPV = In::EPV;
+  constexpr int OSZ = OutBF16 ? 2 : 4;
+  const int row = blockIdx.y;
+  const float* st = P.row_stats + 8 * (int64_t)row;
+  const float S = st[2];
+  RowConst rc;
+  rc.init(st[4], st[5], st[6]);
+  const float delta = rc.delta;
+  const int atop = P.target_top1[row];
+  const float alpha = P.alpha, tau = P.tau;
+  const float wrow = P.grad_loss ? P.grad_loss[row] : 1.f;
+  const float wa = wrow * alpha;
+  const float k0 = wrow * (alpha * ((1.f - delta) - S) + (1.f - alpha));
+  const float kc = wrow * ((1.f - alpha) - alpha * S);
+  const float wce = wrow * (1.f - alpha);
+  const uint4* zrow = (const uint4*)(P.z + (int64_t)row * P.ld_bytes);
+  const uint4* yrow = (const uint4*)(P.y + (int64_t)row * P.ld_bytes);
+  uint8_t* drow = P.dz + (int64_t)row * P.ld_dz_bytes;
+  const int v0 = blockIdx.x * (kThreads * kBwdVecPerThread) + threadIdx.x;
+  uint4 zr[kBwdVecPerThread], yr[kBwdVecPerThread];
+#pragma unroll
+  for (int k = 0; k < kBwdVecPerThread; ++k) {
+    const int vc = min(v0 + k * kThreads, P.nvec - 1);
+    zr[k] = zrow[vc];
+    yr[k] = yrow[vc];
+  }
+#pragma unroll
+  for (int k = 0; k < kBwdVecPerThread; ++k) {
+    opaque(zr[k]);
+    opaque(yr[k]);
+  }
+  if (P.nvec * EPV != P.vocab) {  // uniform: rows whose last vector is partial
+#pragma unroll
+    for (int k = 0; k < kBwdVecPerThread; ++k) {
+      const int vi = v0 + k * kThreads;
+      if (vi == P.nvec - 1) {
+        mask_tail<In>(zr[k], P.vocab - vi * EPV);
+        mask_tail<In>(yr[k], P.vocab - vi * EPV);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kBwdVecPerThread; ++k) {
+    const int vi = v0 + k * kThreads;
+    if (vi < P.nvec) {
+      float x[EPV], w[EPV], o[EPV];
+      In::decode(zr[k], x);
+      In::decode(yr[k], w);
+      // the fused kernel's vector bound, recomputed: same decisions, bit-identical dz
+      float zm = x[0], dm = x[0] - w[0];
+#pragma unroll
+      for (int e = 1; e < EPV; ++e) {
+        zm = fmaxf(zm, x[e]);
+        dm = fmaxf(dm, x[e] - w[e]);
+      }
+      const bool slow = rc.p(zm) * fmaxf(dm - delta, 0.f) > tau;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const float p = rc.p(x[e]);
+        const float d = x[e] - w[e];
+        float coef = __builtin_fmaf(wa, d, k0);
+        if (slow) coef = (p * (d - delta) > tau) ? kc : coef;
+        o[e] = p * coef;
+      }
+      const int g0 = vi * EPV;
+      if (atop >= g0 && atop < g0 + EPV) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) o[e] = (g0 + e == atop) ? o[e] - wce : o[e];
+      }
+      uint8_t* dst = drow + (int64_t)g0 * OSZ;
+      if (g0 + EPV <= P.vocab) {
+        store_vec<OutBF16, EPV>(dst, o);
+      } else {
+        store_partial<OutBF16, EPV>(dst, o, P.vocab - g0);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- accept length per packed block
+
+__global__ void __launch_bounds__(kThreads) k_accept(AcceptParams P) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= P.n_blocks) return;
+  const int start = P.offsets[b], end = P.offsets[b + 1];
+  uint32_t fl = 0;
+  int acc = 0;
+  if (start < 0 || end < start || end > P.n_rows) {
+    fl |= kFlagBadOffsets;
+  } else {
+    int lb = P.L[b];
+    if (lb < 0) {
+      fl |= kFlagNegL;
+      lb = 0;
+    }
+    const int n = min(lb, end - start);
+    while (acc < n && P.draft_top1[start + acc] == P.target_top1[start + acc]) ++acc;
+  }
+  P.accept_len[b] = acc;
+  if (fl) atomicOr(P.flags, fl);
+}
+
+__global__ void k_fill_u32(uint32_t* dst, uint32_t value, size_t count) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x) {
+    dst[i] = value;
+  }
+}
+
+// ---------------------------------------------------------------- instantiation tables
+
+template <int MODE>
+void* team_kernel(int in_bf16, int out_bf16, int K) {
+  if (MODE != kFused) out_bf16 = 0;
+  if (in_bf16) {
+    if (out_bf16) return K == 1 ? (void*)k_team<BF16In, true, 1, MODE> : (void*)k_team<BF16In, true, 5, MODE>;
+    return K == 1 ? (void*)k_team<BF16In, false, 1, MODE> : (void*)k_team<BF16In, false, 5, MODE>;
+  }
+  if (out_bf16) return K == 1 ? (void*)k_team<F32In, true, 1, MODE> : (void*)k_team<F32In, true, 5, MODE>;
+  return K == 1 ? (void*)k_team<F32In, false, 1, MODE> : (void*)k_team<F32In, false, 5, MODE>;
+}
+
+void* team_kernel_any(int mode, int in_bf16, int out_bf16, int K) {
+  switch (mode) {
+    case kFused: return team_kernel<kFused>(in_bf16, out_bf16, K);
+    case kForward: return team_kernel<kForward>(in_bf16, out_bf16, K);
+    default: return team_kernel<kTop1>(in_bf16, out_bf16, K);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_team(const TeamParams& p, int mode, int in_bf16, int out_bf16, int K, int grid, hipStream_t s) {
+  void* fn = team_kernel_any(mode, in_bf16, out_bf16, K);
+  TeamParams copy = p;
+  void* args[] = {&copy};
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
+hipError_t team_occupancy(int mode, int in_bf16, int out_bf16, int K, int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, team_kernel_any(mode, in_bf16, out_bf16, K),
+                                                      kThreads, 0);
+}
+
+hipError_t launch_bwd(const BwdParams& p, int in_bf16, int out_bf16, hipStream_t s) {
+  const int per_block = kThreads * kBwdVecPerThread;
+  dim3 grid((p.nvec + per_block - 1) / per_block, p.n_rows);
+  BwdParams copy = p;
+  void* args[] = {&copy};
+  void* fn;
+  if (in_bf16) fn = out_bf16 ? (void*)k_bwd<BF16In, true> : (void*)k_bwd<BF16In, false>;
+  else fn = out_bf16 ? (void*)k_bwd<F32In, true> : (void*)k_bwd<F32In, false>;
+  return hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_accept(const AcceptParams& p, hipStream_t s) {
+  dim3 grid((p.n_blocks + kThreads - 1) / kThreads);
+  AcceptParams copy = p;
+  void* args[] = {&copy};
+  return hipLaunchKernel((void*)k_accept, grid, dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, size_t count, hipStream_t s) {
+  size_t blocks = (count + kThreads - 1) / kThreads;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(kThreads), 0, s, dst, value, count);
+  return hipGetLastError();
+}
+
+}  // namespace opd

@@ -1,0 +1,161 @@
+/*
+ * opd.h — C ABI of the MI355X (gfx950) on-policy-distillation loss / verification library.
+ *
+ * What it computes (one "row" = one drafted position, V = vocabulary size):
+ *   p = softmax(z) over the drafter logits z, q = softmax(y) over the target logits y,
+ *   a = argmax y (target top-1, lowest index on ties), d = argmax z (draft top-1, same rule),
+ *   loss = alpha * sum_v min(p_v (log p_v - log q_v), tau) + (1 - alpha) * (-log p_a)
+ *   dz   = w * d loss / d z   (no gradient to y; w = grad_loss[row], default 1)
+ *   accept_len[b] = longest prefix of packed block b, within clamp(L_b, 0, n_b) rows, on which
+ *                   d == a.
+ * Sources, by page title and section:
+ *   - "AdaFlash: Adaptive Speculative Decoding with Online Self-Improvement for High-Concurrency
+ *     LLM Inference" (besthub.dev article), section "1. On-Policy Distillation (OPD) for Domain
+ *     Adaptation": reverse KL (drafter || target) plus top-1 hard labels from the target; each
+ *     vocabulary term of the reverse KL is clipped before the sum.
+ *   - same article, section "2. Adaptive Length Head for Token-Level Variance": blocks of k = 16
+ *     drafted positions, verification budget set by a predicted acceptance length L.
+ *   - same article, section "Infrastructure: Async Training & Variable-Length Batching": requests
+ *     with different verification lengths packed contiguously into one batch (int32 offsets here).
+ *   - "AdaFlash: Adaptive Speculative Decoding via On-Policy Distilled Diffusion Drafters"
+ *     (project README page), section "Released Checkpoint": the drafter's loss is a mixture of
+ *     reverse KL and the hard-label term.
+ * alpha and tau are explicit arguments (the pages do not fix them). Temperature is 1; callers
+ * pre-scale logits for other temperatures. The clip is an upper clip only; at t_v == tau the term
+ * counts as unclipped (its gradient passes).
+ *
+ * Conventions shared by every call
+ *   - Array arguments are DEVICE pointers, owned by the caller; the library allocates nothing and
+ *     keeps no device state apart from what lives in the caller's workspace.
+ *   - Logit matrices are row-major [n_rows, ld] with ld >= vocab; the caller's buffer must span
+ *     n_rows * ld elements (the pad [vocab, ld) of a row may be read, never written). Base pointer
+ *     and row pitch (ld * element size) must be multiples of 16 bytes.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the legacy default stream) and return
+ *     without synchronising. Host-checkable errors return before any HIP call is made.
+ *   - Results are deterministic: the same inputs give bit-identical outputs (no floating-point
+ *     atomics; every reduction has a fixed order).
+ *   - Preconditions on values: finite logits with |logit| <= 1e4. Other values give unspecified
+ *     numbers but every kernel still terminates.
+ *   - A workspace of opd_workspace_size() bytes, zero-filled once when first allocated, must be
+ *     passed to every call; calls that share a workspace must not run concurrently.
+ *   - Device-side content problems (negative L, malformed offsets, a cross-workgroup wait that
+ *     exceeded its bound) set bits in a sticky flag word inside the workspace, read with
+ *     opd_read_flags().
+ */
+#ifndef OPD_MI355X_H
+#define OPD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { OPD_F32 = 0, OPD_BF16 = 1 } opd_dtype_t;
+
+typedef enum {
+  OPD_OK = 0,
+  OPD_ERR_NULL = 1,       /* a required pointer is NULL                                       */
+  OPD_ERR_SHAPE = 2,      /* n_rows < 0, vocab <= 0 or > 524288, ld < vocab, n_blocks < 0    */
+  OPD_ERR_DTYPE = 3,      /* dtype value not in opd_dtype_t                                   */
+  OPD_ERR_ALIGN = 4,      /* base pointer or row pitch not a multiple of 16 bytes              */
+  OPD_ERR_PARAM = 5,      /* alpha outside [0, 1] or NaN, tau NaN                              */
+  OPD_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than opd_workspace_size()              */
+  OPD_ERR_HIP = 7         /* a HIP call failed; opd_last_error() has the HIP error text       */
+} opd_status_t;
+
+/* Bits of the sticky device flag word (see opd_read_flags). */
+#define OPD_FLAG_NEG_L 1u        /* some block had L < 0 (treated as 0)                         */
+#define OPD_FLAG_BAD_OFFSETS 2u  /* some block had decreasing / out-of-range offsets (accept 0)   */
+#define OPD_FLAG_SPIN_TIMEOUT 4u /* a cross-workgroup wait exceeded its bound: outputs invalid    */
+
+/* Packed verification blocks ("Infrastructure: ... Variable-Length Batching"): block b owns rows
+ * offsets[b] .. offsets[b+1]-1; L[b] is the length head's predicted verification length.
+ * The struct lives on the host; both arrays are device arrays. */
+typedef struct {
+  const int32_t* offsets; /* [n_blocks + 1], expected offsets[0] = 0, non-decreasing, <= n_rows */
+  const int32_t* L;       /* [n_blocks]                                                          */
+  int32_t n_blocks;
+} opd_blocks_t;
+
+/* Bytes of workspace every call needs (independent of the problem size). */
+size_t opd_workspace_size(void);
+
+/*
+ * Forward: per-row loss and the statistics the backward pass reuses.
+ *   z, y        [n_rows, ld] drafter / target logits of dtype dt.
+ *   loss        [n_rows] float32 out.
+ *   target_top1 [n_rows] int32 out (argmax y); draft_top1 [n_rows] int32 out, may be NULL.
+ *   row_stats   [n_rows][8] float32 out: (LSE(z), LSE(y), S, clipped reverse KL, max z,
+ *               log sum_v e^(z_v - max z), LSE(z) - LSE(y), cross entropy), where
+ *               S = sum_v p_v [t_v <= tau] (log p_v - log q_v + 1) is the row constant of the
+ *               gradient. Entries 4..6 carry LSE(z) and the LSE difference at full precision for
+ *               the backward pass.
+ * Errors: OPD_ERR_NULL (z, y, loss, target_top1, row_stats), OPD_ERR_SHAPE, OPD_ERR_DTYPE,
+ * OPD_ERR_ALIGN, OPD_ERR_PARAM, OPD_ERR_WORKSPACE, OPD_ERR_HIP.
+ */
+opd_status_t opd_loss_fwd(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+                          int64_t ld, float alpha, float tau, float* loss, int32_t* target_top1,
+                          int32_t* draft_top1, float* row_stats, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * Backward: dz = grad_loss[row] * d loss_row / d z_row from the forward's row_stats and
+ * target_top1 (one streaming pass: read z and y, write dz).
+ *   grad_loss   [n_rows] float32, may be NULL (then 1 for every row).
+ *   dz          [n_rows, ld_dz] of dtype dz_dt (bf16 is rounded to nearest even); must not alias
+ *               z or y. Pitch ld_dz * size must be a multiple of 16 bytes, ld_dz >= vocab.
+ * Errors: as opd_loss_fwd, plus OPD_ERR_NULL for row_stats / target_top1 / dz.
+ */
+opd_status_t opd_loss_bwd(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+                          int64_t ld, float alpha, float tau, const float* row_stats,
+                          const int32_t* target_top1, const float* grad_loss, void* dz,
+                          opd_dtype_t dz_dt, int64_t ld_dz, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * Greedy verification ("2. Adaptive Length Head ..."): computes both top-1 arrays from the logits
+ * and the accepted-prefix length of every packed block.
+ *   target_top1, draft_top1 [n_rows] int32 out; accept_len [n_blocks] int32 out.
+ * Errors: OPD_ERR_NULL (z, y, blocks and its arrays when n_blocks > 0, the three outputs),
+ * OPD_ERR_SHAPE, OPD_ERR_DTYPE, OPD_ERR_ALIGN, OPD_ERR_WORKSPACE, OPD_ERR_HIP.
+ */
+opd_status_t verify_accept_len(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows,
+                               int64_t vocab, int64_t ld, const opd_blocks_t* blocks,
+                               int32_t* target_top1, int32_t* draft_top1, int32_t* accept_len,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Fused forward + backward + verification: everything above in one pass over the logits (each of
+ * z and y read once from HBM, dz written once), then the per-block accept lengths.
+ *   blocks may be NULL (no verification; accept_len ignored).
+ * Outputs and errors: the union of the three calls above.
+ */
+opd_status_t opd_fused_fwd_bwd_verify(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows,
+                                      int64_t vocab, int64_t ld, const opd_blocks_t* blocks,
+                                      float alpha, float tau, const float* grad_loss, float* loss,
+                                      int32_t* target_top1, int32_t* draft_top1, float* row_stats,
+                                      void* dz, opd_dtype_t dz_dt, int64_t ld_dz,
+                                      int32_t* accept_len, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
+
+/* Reads the sticky device flag word of a workspace (synchronises `stream`); clears it when
+ * `clear` is non-zero. Errors: OPD_ERR_NULL, OPD_ERR_WORKSPACE, OPD_ERR_HIP. */
+opd_status_t opd_read_flags(void* ws, size_t ws_bytes, int clear, uint32_t* flags, hipStream_t stream);
+
+/* Debug knob for tests of the failure path: caps every cross-workgroup wait at `spins` polls
+ * (0 restores the default bound). Affects launches made after the call, process-wide. */
+void opd_set_spin_limit(uint32_t spins);
+
+/* Static description of a status code, and the detail text of the last error on this thread. */
+const char* opd_status_string(opd_status_t s);
+const char* opd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OPD_MI355X_H */

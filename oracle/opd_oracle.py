@@ -42,6 +42,7 @@ import numpy as np
 __all__ = [
     "logsumexp",
     "top1",
+    "top1_rows",
     "row_forward",
     "row_grad",
     "accept_lengths",
@@ -81,6 +82,15 @@ def top1(x) -> int:
     draft. numpy.argmax returns the first occurrence of the maximum, which is the lowest index.
     """
     return int(np.argmax(_as_f64(x)))
+
+
+def top1_rows(x) -> np.ndarray:
+    """``top1`` of every row of a [rows, V] array of exactly represented values (float32 or float64
+    hold bf16 and fp32 inputs exactly, so the argmax is the same in either)."""
+    x = np.asarray(x)
+    if x.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    return np.argmax(x, axis=1).astype(np.int64)
 
 
 def row_forward(z, y, alpha: float, tau: float) -> dict:

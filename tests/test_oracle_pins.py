@@ -56,6 +56,15 @@ def test_top1_lowest_index_brute_force():
         assert O.top1(x) == bi
 
 
+def test_top1_rows_matches_rowwise_brute_force():
+    rng = np.random.default_rng(1)
+    x = rng.integers(-2, 2, size=(300, 17)).astype(np.float32)
+    got = O.top1_rows(x)
+    for i in range(x.shape[0]):
+        first = min(j for j in range(17) if x[i, j] == x[i].max())
+        assert got[i] == first
+
+
 # ---------------------------------------------------------------- loss: library special cases
 
 
