@@ -137,7 +137,12 @@ def main():
     ap.add_argument("--workload", default="train", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-blocks", type=int, default=512, help="blocks of the workload timed on the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="for rocprofv3 counter runs: no CPU baseline, and after the timed steps a plain "
+                         "1 GiB device copy (torch copy_) whose FETCH_SIZE / WRITE_SIZE calibrate the counters")
     args = ap.parse_args()
+    if args.profile:
+        args.no_cpu_baseline = True
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (rows shard across GPUs "
@@ -209,6 +214,15 @@ def main():
     if opd.read_flags(ws, clear=True) != 0:
         print("[bench] device flags raised during the timed region", file=sys.stderr)
         sys.exit(1)
+
+    if args.profile:
+        # calibration copy: 1 GiB read + 1 GiB written by a plain copy kernel
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms_per_step = wall * 1e3 / args.steps
     rows_per_s = n / (ms_per_step * 1e-3)

@@ -42,7 +42,8 @@ _lib = None
 
 
 def library_path() -> str:
-    return _build.lib_path()
+    """The in-tree build, or the file named by OPD_MI355X_LIB (for trying alternative builds)."""
+    return os.environ.get("OPD_MI355X_LIB") or _build.lib_path()
 
 
 def load_library(require_torch_runtime: bool = True) -> ctypes.CDLL:

@@ -58,8 +58,10 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 struct F32In {
   static constexpr int EPV = 4;
-  // -9.95e29: contributes 0 to every sum and never wins a max (inputs satisfy |logit| <= 1e4)
-  static constexpr uint32_t kSentinel = 0xF1490000u;
+  // -32768 (exact in fp32 and bf16): never a maximum and e^(s - max) underflows to 0, because inputs
+  // satisfy |logit| <= 1e4; small enough that s log2(e) keeps a tiny absolute rounding error (a
+  // vector made only of sentinels is reduced relative to its own maximum, the sentinel itself).
+  static constexpr uint32_t kSentinel = 0xC7000000u;
   __device__ static __forceinline__ void decode(const uint4& v, float (&x)[EPV]) {
     x[0] = __uint_as_float(v.x);
     x[1] = __uint_as_float(v.y);
@@ -73,7 +75,7 @@ struct F32In {
 
 struct BF16In {
   static constexpr int EPV = 8;
-  static constexpr uint32_t kSentinel = 0xF149F149u;
+  static constexpr uint32_t kSentinel = 0xC700C700u;  // two bf16 -32768 (see F32In)
   __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
   __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
   __device__ static __forceinline__ void decode(const uint4& v, float (&x)[EPV]) {
@@ -103,6 +105,19 @@ __device__ __forceinline__ void mask_tail(uint4& v, int nvalid) {
 
 __device__ __forceinline__ uint4 splat4(uint32_t s) { return make_uint4(s, s, s, s); }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (nontemporal) 16-byte load / store: the logits are read once and dz written once, so
+// they are marked not to be kept in the caches.
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt(uint8_t* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4 v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 // ---------------------------------------------------------------- output formats
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -117,15 +132,15 @@ template <bool OutBF16, int EPV>
 __device__ __forceinline__ void store_vec(uint8_t* dst, const float (&o)[EPV]) {
   if constexpr (OutBF16) {
     if constexpr (EPV == 8) {
-      *(uint4*)dst = make_uint4(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
-                                pack_bf16(o[6], o[7]));
+      store_nt(dst, pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7]));
     } else {
       *(uint2*)dst = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
     }
   } else {
 #pragma unroll
     for (int q = 0; q < EPV / 4; ++q) {
-      *(float4*)(dst + 16 * q) = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+      store_nt(dst + 16 * q, __float_as_uint(o[4 * q]), __float_as_uint(o[4 * q + 1]), __float_as_uint(o[4 * q + 2]),
+               __float_as_uint(o[4 * q + 3]));
     }
   }
 }
@@ -228,14 +243,61 @@ __device__ __forceinline__ bool exchange(Shared& sh, const TeamParams& P, int te
   return sh.err == 0;
 }
 
+// ---------------------------------------------------------------- wave reductions (DPP)
+
+// Full-wave reductions on the DPP crossbar (quad_perm, row mirrors, row broadcasts): six ALU ops
+// instead of six LDS-permute round trips. The result is read from lane 63 and is wave-uniform.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_mov(int v, int identity) {
+  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ float dppf(float v, float id, int which) {
+  switch (which) {
+    case 0: return __int_as_float(dpp_mov<0xB1, 0xF>(__float_as_int(v), __float_as_int(id)));
+    case 1: return __int_as_float(dpp_mov<0x4E, 0xF>(__float_as_int(v), __float_as_int(id)));
+    case 2: return __int_as_float(dpp_mov<0x141, 0xF>(__float_as_int(v), __float_as_int(id)));
+    case 3: return __int_as_float(dpp_mov<0x140, 0xF>(__float_as_int(v), __float_as_int(id)));
+    case 4: return __int_as_float(dpp_mov<0x142, 0xA>(__float_as_int(v), __float_as_int(id)));
+    default: return __int_as_float(dpp_mov<0x143, 0xC>(__float_as_int(v), __float_as_int(id)));
+  }
+}
+__device__ __forceinline__ int dppi(int v, int id, int which) {
+  switch (which) {
+    case 0: return dpp_mov<0xB1, 0xF>(v, id);
+    case 1: return dpp_mov<0x4E, 0xF>(v, id);
+    case 2: return dpp_mov<0x141, 0xF>(v, id);
+    case 3: return dpp_mov<0x140, 0xF>(v, id);
+    case 4: return dpp_mov<0x142, 0xA>(v, id);
+    default: return dpp_mov<0x143, 0xC>(v, id);
+  }
+}
+__device__ __forceinline__ float uniform_f(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wmax(float v) {
+#pragma unroll
+  for (int s = 0; s < 6; ++s) v = fmaxf(v, dppf(v, kNegInf, s));
+  return uniform_f(v);
+}
+__device__ __forceinline__ float wsum(float v) {
+#pragma unroll
+  for (int s = 0; s < 6; ++s) v = v + dppf(v, 0.f, s);
+  return uniform_f(v);
+}
+__device__ __forceinline__ int wmin(int v) {
+#pragma unroll
+  for (int s = 0; s < 6; ++s) v = min(v, dppi(v, kBig, s));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 // ---------------------------------------------------------------- per-row constants
 
 // Probability of a logit x under the row's softmax, p(x) = exp(x - LSE(z)), evaluated as
 // exp2(fma(x, log2 e, -c_hi) - c_lo) with c_hi + c_lo = M_z log2 e + log2 S_z carried in two floats:
 // fma forms x log2 e - c_hi with a single rounding, so p keeps full fp32 relative accuracy even for
 // logits in the thousands (a single fp32 constant LSE log2 e would be off by up to half an ulp of
-// ~1.4e4, i.e. 1e-3 in p). The same function, from the same stored floats, is used by the fused
-// kernel and by the separate backward kernel, so their clip decisions agree bit for bit.
+// ~1.4e4, i.e. 1e-3 in p). This canonical p is used for every clip decision, in the fused kernel
+// and in the separate backward kernel, from the same stored floats, so their decisions agree.
 struct RowConst {
   float c_hi, c_lo;  // p(x) = exp2(fma(x, log2e, -c_hi) - c_lo)
   float delta;       // LSE(z) - LSE(y)
@@ -247,7 +309,49 @@ struct RowConst {
   __device__ __forceinline__ float p(float x) const {
     return exp2_fast(__builtin_fmaf(x, kLog2e, -c_hi) - c_lo);
   }
+  // p(x) 2^c_lo: dz folds the factor 2^-c_lo into its coefficients (one op less per element)
+  __device__ __forceinline__ float e(float x) const { return exp2_fast(__builtin_fmaf(x, kLog2e, -c_hi)); }
 };
+
+// dz_v = w p_v (alpha (z_v - y_v) + alpha (1 - delta - S) + 1 - alpha) for an unclipped term,
+// w p_v (1 - alpha - alpha S) for a clipped one, minus w (1 - alpha) at the target top-1.
+struct DzConst {
+  float wa, k0, kc;  // scaled by 2^-c_lo (see RowConst::e)
+  float wce;
+  __device__ __forceinline__ void init(const RowConst& rc, float S, float alpha, float w) {
+    const float f = exp2_fast(-rc.c_lo);
+    wa = (w * alpha) * f;
+    k0 = (w * (alpha * ((1.f - rc.delta) - S) + (1.f - alpha))) * f;
+    kc = (w * ((1.f - alpha) - alpha * S)) * f;
+    wce = w * (1.f - alpha);
+  }
+};
+
+// dz of one 16-byte vector. `slow` marks a lane whose vector may hold clipped terms (its bound
+// exceeds tau); `any_slow` is the wave-uniform OR of it, so the clip tests run only in waves that
+// need them. Shared by the fused and the backward kernels (bit-identical results).
+template <int EPV>
+__device__ __forceinline__ void dz_vector(const float (&x)[EPV], const float (&w)[EPV], bool slow, bool any_slow,
+                                          const RowConst& rc, const DzConst& dc, float tau, float (&o)[EPV]) {
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) o[e] = rc.e(x[e]) * __builtin_fmaf(dc.wa, x[e] - w[e], dc.k0);
+  if (any_slow) {
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const bool clip = slow && (rc.p(x[e]) * ((x[e] - w[e]) - rc.delta) > tau);
+      o[e] = clip ? rc.e(x[e]) * dc.kc : o[e];
+    }
+  }
+}
+
+template <int EPV>
+__device__ __forceinline__ void fix_target(float (&o)[EPV], int g0, int atop, float wce) {
+  const unsigned rel = (unsigned)(atop - g0);
+  if (rel < (unsigned)EPV) {
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) o[e] = ((unsigned)e == rel) ? o[e] - wce : o[e];
+  }
+}
 
 // Keeps the packed inputs opaque between phases so that the compiler re-decodes them (1 VALU op per
 // element) instead of keeping decoded fp32 copies alive across the exchanges (which doubles the VGPR
@@ -263,16 +367,34 @@ __device__ __forceinline__ void fence_vals(float& a, float& b, float& c, float& 
   __asm__ volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
+// Requests this thread's K vectors of a row's chunk of z and y (nontemporal, indices clamped into
+// the chunk so that every lane loads valid memory and no branch separates the loads).
+template <int K>
+__device__ __forceinline__ void load_chunk(uint4 (&zr)[K], uint4 (&yr)[K], const TeamParams& P, int row, int tv,
+                                           int cv1) {
+  const uint4* zrow = (const uint4*)(P.z + (int64_t)row * P.ld_bytes);
+  const uint4* yrow = (const uint4*)(P.y + (int64_t)row * P.ld_bytes);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int vc = min(tv + k * kThreads, cv1 - 1);
+    zr[k] = load_nt(zrow + vc);
+    yr[k] = load_nt(yrow + vc);
+  }
+}
+
+// Workgroup-wide combine of wave-uniform values through LDS (4 waves).
+__device__ __forceinline__ void put4(Shared& sh, int slot, float v) {
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6][slot] = v;
+}
+
 // ---------------------------------------------------------------- the row-team kernel
 
-template <class In, bool OutBF16, int K, int MODE>
+template <class In, bool OutBF16, int K, int MODE, bool PF>
 __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
   constexpr int EPV = In::EPV;
   constexpr int OSZ = OutBF16 ? 2 : 4;
   __shared__ Shared sh;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   const int b = blockIdx.x;
   int team, chunk;
   if (P.xcd_map) {
@@ -285,10 +407,19 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
   }
   const int cv0 = chunk * P.chunk_vec;
   const int cv1 = min(cv0 + P.chunk_vec, P.nvec);
+  const int clen = cv1 - cv0;  // vectors in this chunk (uniform)
   const float alpha = P.alpha, tau = P.tau;
   const bool tail_chunk = (cv1 == P.nvec) && (P.nvec * EPV != P.vocab);
   if (tid == 0) sh.err = 0;
 
+  // Rows may be double-buffered in registers (PF): the next row's chunk is then requested at the
+  // top of each row pass so that its latency overlaps this row's work.
+  uint4 zr[K], yr[K];
+  if constexpr (PF) {
+    int tv = cv0 + tid;
+    __asm__ volatile("" : "+v"(tv));
+    if (team < P.n_rows) load_chunk<K>(zr, yr, P, team, tv, cv1);
+  }
   int iter = 0;
   for (int row = team; row < P.n_rows; row += P.n_teams, ++iter) {
     __syncthreads();
@@ -296,29 +427,27 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
     // index and bounds test out of the row loop and keeps them all in registers.
     int tv = cv0 + tid;
     __asm__ volatile("" : "+v"(tv));
-    const uint4* zrow = (const uint4*)(P.z + (int64_t)row * P.ld_bytes);
-    const uint4* yrow = (const uint4*)(P.y + (int64_t)row * P.ld_bytes);
-    // All K loads of z and y are issued back to back (indices clamped into the chunk, so no branch
-    // and no wait between them); slots past the chunk end are replaced by the sentinel afterwards.
-    uint4 zr[K], yr[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int vc = min(tv + k * kThreads, cv1 - 1);
-      zr[k] = zrow[vc];
-      yr[k] = yrow[vc];
+    const int next_row = row + P.n_teams;
+    uint4 nz[K], ny[K];
+    if constexpr (PF) {
+      if (next_row < P.n_rows) load_chunk<K>(nz, ny, P, next_row, tv, cv1);
+    } else {
+      load_chunk<K>(zr, yr, P, row, tv, cv1);
     }
 #pragma unroll
-    for (int k = 0; k < K; ++k) {  // pins the loads here (else they are sunk into branches)
+    for (int k = 0; k < K; ++k) {  // the current row must be in registers from here on
       opaque(zr[k]);
       opaque(yr[k]);
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const bool in = tv + k * kThreads < cv1;
-      zr[k] = in ? zr[k] : splat4(In::kSentinel);
-      yr[k] = in ? yr[k] : splat4(In::kSentinel);
+      if ((k + 1) * kThreads > clen) {  // uniform: only slots that can run past the chunk end
+        const bool in = tv + k * kThreads < cv1;
+        zr[k] = in ? zr[k] : splat4(In::kSentinel);
+        yr[k] = in ? yr[k] : splat4(In::kSentinel);
+      }
     }
-    if (tail_chunk) {  // wave-uniform: only the chunk holding a partial last vector
+    if (tail_chunk) {  // uniform: only the chunk holding a partial last vector
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const int vi = tv + k * kThreads;
@@ -329,40 +458,62 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
       }
     }
 
-    // ---- phase A1: maxima (per vector of z, per lane of y)
-    float zmv[K];
-    float lzmax = kNegInf, lymax = kNegInf;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      float x[EPV], w[EPV];
-      In::decode(zr[k], x);
-      In::decode(yr[k], w);
-      float a = x[0], c = w[0];
-#pragma unroll
-      for (int e = 1; e < EPV; ++e) {
-        a = fmaxf(a, x[e]);
-        c = fmaxf(c, w[e]);
-      }
-      zmv[k] = a;
-      lzmax = fmaxf(lzmax, a);
-      lymax = fmaxf(lymax, c);
-      fence_vals(lzmax, lymax);
-    }
-    {
-      const float a = wave_max(lzmax), c = wave_max(lymax);
-      if (lane == 0) {
-        sh.red[wave][0] = a;
-        sh.red[wave][1] = c;
-      }
-    }
-    __syncthreads();
-    const float m_z = fmaxf(fmaxf(sh.red[0][0], sh.red[1][0]), fmaxf(sh.red[2][0], sh.red[3][0]));
-    const float m_y = fmaxf(fmaxf(sh.red[0][1], sh.red[1][1]), fmaxf(sh.red[2][1], sh.red[3][1]));
+    // ---- phase A (one pass): per 8-element vector, its z max, y max and max(z - y), and the sums
+    // E_k = sum e^(z - zmax_k), B_k = sum e^(z - zmax_k)(z - y), sum e^(y - ymax_k) relative to that
+    // vector's own maxima (so no workgroup maximum is needed first). Exponents use
+    // c = fl(max log2 e); the rounding of c is undone once per vector when folding into the lane's
+    // running (max, sum) pairs, and phase B rescales E_k, B_k by 2^(c_k - c_row).
+    float zmv[K], dmv[K], ek[K], bk[K];
+    float lzmax = kNegInf, lymax = kNegInf, lsz = 0.f, lsy = 0.f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       opaque(zr[k]);
       opaque(yr[k]);
+      float x[EPV], w[EPV];
+      In::decode(zr[k], x);
+      In::decode(yr[k], w);
+      float zm = x[0], ym = w[0], dm = x[0] - w[0];
+#pragma unroll
+      for (int e = 1; e < EPV; ++e) {
+        zm = fmaxf(zm, x[e]);
+        ym = fmaxf(ym, w[e]);
+        dm = fmaxf(dm, x[e] - w[e]);
+      }
+      zmv[k] = zm;
+      dmv[k] = dm;
+      if constexpr (MODE != kTop1) {
+        const float cz = zm * kLog2e, cy = ym * kLog2e;
+        float se = 0.f, sb = 0.f, sey = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float ez = exp2_fast(__builtin_fmaf(x[e], kLog2e, -cz));
+          se += ez;
+          sb = __builtin_fmaf(ez, x[e] - w[e], sb);
+          sey += exp2_fast(__builtin_fmaf(w[e], kLog2e, -cy));
+        }
+        ek[k] = se;
+        bk[k] = sb;
+        // fold into the lane's (max, sum) pairs; exponent offsets: (max_k - M) log2e - (rounding of c)
+        const float nz = fmaxf(lzmax, zm), ny = fmaxf(lymax, ym);
+        lsz = __builtin_fmaf(lsz, exp2_fast((lzmax - nz) * kLog2e),
+                             se * exp2_fast((zm - nz) * kLog2e - __builtin_fmaf(zm, kLog2e, -cz)));
+        lsy = __builtin_fmaf(lsy, exp2_fast((lymax - ny) * kLog2e),
+                             sey * exp2_fast((ym - ny) * kLog2e - __builtin_fmaf(ym, kLog2e, -cy)));
+        lzmax = nz;
+        lymax = ny;
+        fence_vals(lzmax, lymax, lsz, lsy);
+        fence_vals(zmv[k], dmv[k], ek[k], bk[k]);
+      } else {
+        lzmax = fmaxf(lzmax, zm);
+        lymax = fmaxf(lymax, ym);
+        fence_vals(lzmax, lymax);
+      }
     }
+    put4(sh, 0, wmax(lzmax));
+    put4(sh, 1, wmax(lymax));
+    __syncthreads();
+    const float m_z = fmaxf(fmaxf(sh.red[0][0], sh.red[1][0]), fmaxf(sh.red[2][0], sh.red[3][0]));
+    const float m_y = fmaxf(fmaxf(sh.red[0][1], sh.red[1][1]), fmaxf(sh.red[2][1], sh.red[3][1]));
 
     // ---- lowest index of each chunk maximum: only lanes holding it scan, from the top down with
     // selects, so the last hit is the lowest index
@@ -372,6 +523,7 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
       int code = 0;
 #pragma unroll
       for (int k = K - 1; k >= 0; --k) {
+        opaque(zr[k]);
         float x[EPV];
         In::decode(zr[k], x);
 #pragma unroll
@@ -383,6 +535,8 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
       int code = 0;
 #pragma unroll
       for (int k = K - 1; k >= 0; --k) {
+        opaque(zr[k]);
+        opaque(yr[k]);
         float x[EPV], w[EPV];
         In::decode(zr[k], x);
         In::decode(yr[k], w);
@@ -395,74 +549,37 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
       }
       iy = (tv + (code / EPV) * kThreads) * EPV + code % EPV;
     }
-
-    // ---- phase A2: exponential sums relative to the chunk maxima. E_k, B_k per vector are kept:
-    // phase B turns them into the unclipped part of S and of the reverse KL without cancellation.
-    float dmv[K], ek[K], bk[K];
-    float sy = 0.f;
-    float cz_hi = 0.f, cz_lo = 0.f, cy_lo = 0.f;
-    if constexpr (MODE != kTop1) {
-      cz_hi = m_z * kLog2e;
-      cz_lo = __builtin_fmaf(m_z, kLog2e, -cz_hi);
-      const float cy_hi = m_y * kLog2e;
-      cy_lo = __builtin_fmaf(m_y, kLog2e, -cy_hi);
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        opaque(zr[k]);
-        opaque(yr[k]);
-        float x[EPV], w[EPV];
-        In::decode(zr[k], x);
-        In::decode(yr[k], w);
-        float dm = kNegInf, se = 0.f, sb = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const float d = x[e] - w[e];
-          dm = fmaxf(dm, d);
-          const float ez = exp2_fast(__builtin_fmaf(x[e], kLog2e, -cz_hi));
-          se += ez;
-          sb = __builtin_fmaf(ez, d, sb);
-          sy += exp2_fast(__builtin_fmaf(w[e], kLog2e, -cy_hi));
-        }
-        fence_vals(dm, se, sb, sy);
-        dmv[k] = dm;
-        ek[k] = se;
-        bk[k] = sb;
-      }
-    }
-    float sz = 0.f;
-#pragma unroll
-    for (int k = 0; k < K; ++k) sz += (MODE != kTop1) ? ek[k] : 0.f;
     {
-      sz = wave_sum(sz);
-      sy = wave_sum(sy);
-      iz = wave_min(iz);
-      wave_min_pair(iy, zat);
-      if (lane == 0) {
-        sh.red[wave][2] = sz;
-        sh.red[wave][3] = sy;
-        sh.red[wave][5] = zat;
-        sh.ired[wave][0] = iz;
-        sh.ired[wave][1] = iy;
+      const int wiz = wmin(iz);
+      const int wiy = wmin(iy);
+      const float wza = wsum(iy == wiy ? zat : 0.f);  // the lane that owns the index (unique)
+      if constexpr (MODE != kTop1) {
+        // chunk sums relative to the chunk maxima (lane pairs rescaled exactly: bf16/fp32 maxima)
+        put4(sh, 2, wsum(lsz * exp2_fast((lzmax - m_z) * kLog2e)));
+        put4(sh, 3, wsum(lsy * exp2_fast((lymax - m_y) * kLog2e)));
       }
+      put4(sh, 4, __int_as_float(wiz));
+      put4(sh, 5, __int_as_float(wiy));
+      put4(sh, 6, wza);
     }
     __syncthreads();
     if (tid == 0) {
-      float tsz = (sh.red[0][2] + sh.red[1][2]) + (sh.red[2][2] + sh.red[3][2]);
-      float tsy = (sh.red[0][3] + sh.red[1][3]) + (sh.red[2][3] + sh.red[3][3]);
-      float tz = 0.f;
+      const float tsz = (sh.red[0][2] + sh.red[1][2]) + (sh.red[2][2] + sh.red[3][2]);
+      const float tsy = (sh.red[0][3] + sh.red[1][3]) + (sh.red[2][3] + sh.red[3][3]);
       int tiz = kBig, tiy = kBig;
+      float tz = 0.f;
       for (int q = 0; q < 4; ++q) {
-        tiz = min(tiz, sh.ired[q][0]);
-        if (sh.ired[q][1] < tiy) {
-          tiy = sh.ired[q][1];
-          tz = sh.red[q][5];
+        tiz = min(tiz, __float_as_int(sh.red[q][4]));
+        const int qi = __float_as_int(sh.red[q][5]);
+        if (qi < tiy) {
+          tiy = qi;
+          tz = sh.red[q][6];
         }
       }
-      // undo the rounding of the exponent offsets: sums become sum_v e^(x_v - m) exactly scaled
       sh.out[0] = m_z;
-      sh.out[1] = tsz * exp2_fast(-cz_lo);
+      sh.out[1] = tsz;
       sh.out[2] = m_y;
-      sh.out[3] = tsy * exp2_fast(-cy_lo);
+      sh.out[3] = tsy;
       sh.out[4] = __int_as_float(tiz);
       sh.out[5] = __int_as_float(tiy);
       sh.out[6] = tz;
@@ -474,28 +591,39 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
       if (!exchange<kStage1Units>(sh, P, team, chunk, 0, flag1, true)) break;
     }
 
-    // ---- combine the G chunk partials in chunk order (identical in every member)
-    float Mz = kNegInf, My = kNegInf;
-    float Sz = 0.f, Sy = 0.f, za = 0.f;
-    int dtop = kBig, atop = kBig;
+    // ---- combine the G chunk partials (each lane takes chunks lane, lane+64, ... in order, then a
+    // fixed DPP tree: identical in every member, deterministic)
+    float Mz, My, Sz, Sy, za;
+    int dtop, atop;
     if (P.G > 1) {
-      for (int c = 0; c < P.G; ++c) {
-        Mz = fmaxf(Mz, __uint_as_float(sh.rx[c * kStage1Units + 0]));
-        My = fmaxf(My, __uint_as_float(sh.rx[c * kStage1Units + 2]));
+      const int lane = tid & 63;
+      float mz = kNegInf, my = kNegInf;
+      for (int c = lane; c < P.G; c += 64) {
+        mz = fmaxf(mz, __uint_as_float(sh.rx[c * kStage1Units + 0]));
+        my = fmaxf(my, __uint_as_float(sh.rx[c * kStage1Units + 2]));
       }
-      for (int c = 0; c < P.G; ++c) {
+      Mz = wmax(mz);
+      My = wmax(my);
+      float lsz = 0.f, lsy = 0.f, lza = 0.f;
+      int liz = kBig, liy = kBig;
+      for (int c = lane; c < P.G; c += 64) {
         const uint32_t* u = sh.rx + c * kStage1Units;
         const float mzc = __uint_as_float(u[0]), myc = __uint_as_float(u[2]);
         if constexpr (MODE != kTop1) {
-          Sz = __builtin_fmaf(__uint_as_float(u[1]), exp2_fast((mzc - Mz) * kLog2e), Sz);
-          Sy = __builtin_fmaf(__uint_as_float(u[3]), exp2_fast((myc - My) * kLog2e), Sy);
+          lsz = __builtin_fmaf(__uint_as_float(u[1]), exp2_fast((mzc - Mz) * kLog2e), lsz);
+          lsy = __builtin_fmaf(__uint_as_float(u[3]), exp2_fast((myc - My) * kLog2e), lsy);
         }
-        if (dtop == kBig && mzc == Mz) dtop = (int)u[4];
-        if (atop == kBig && myc == My) {
-          atop = (int)u[5];
-          za = __uint_as_float(u[6]);
+        if (liz == kBig && mzc == Mz) liz = (int)u[4];
+        if (liy == kBig && myc == My) {
+          liy = (int)u[5];
+          lza = __uint_as_float(u[6]);
         }
       }
+      Sz = (MODE != kTop1) ? wsum(lsz) : 0.f;
+      Sy = (MODE != kTop1) ? wsum(lsy) : 0.f;
+      dtop = wmin(liz);
+      atop = wmin(liy);
+      za = wsum(liy == atop ? lza : 0.f);
     } else {
       Mz = sh.out[0];
       Sz = sh.out[1];
@@ -511,7 +639,6 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
         P.target_top1[row] = atop;
         P.draft_top1[row] = dtop;
       }
-      continue;
     } else {
       const float ln_sz = logf(Sz);
       const float ln_sy = logf(Sy);
@@ -523,16 +650,18 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
       // (same monotone p() and subtraction as the element test), so a vector whose bound is <= tau
       // holds no clipped term and its S / reverse-KL contributions come from E_k, B_k. Vectors near
       // the peak are summed element by element.
-      const float scale = exp2_fast((cz_hi - rc.c_hi) - rc.c_lo);  // e-units of this chunk -> p
       const float one_m_delta = 1.f - delta;
       float s_fast = 0.f, r_fast = 0.f, s_slow = 0.f, r_slow = 0.f;
+      bool slowv[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const float ub = rc.p(zmv[k]) * fmaxf(dmv[k] - delta, 0.f);
-        if (ub <= tau) {
-          s_fast += __builtin_fmaf(one_m_delta, ek[k], bk[k]);
-          r_fast += __builtin_fmaf(-delta, ek[k], bk[k]);
-        } else {
+        slowv[k] = ub > tau;
+        // e-units of vector k (relative to 2^(fl(zmax_k log2e))) -> probabilities
+        const float scale = exp2_fast((zmv[k] * kLog2e - rc.c_hi) - rc.c_lo);
+        s_fast += slowv[k] ? 0.f : scale * __builtin_fmaf(one_m_delta, ek[k], bk[k]);
+        r_fast += slowv[k] ? 0.f : scale * __builtin_fmaf(-delta, ek[k], bk[k]);
+        if (__builtin_amdgcn_ballot_w64(slowv[k])) {
           opaque(zr[k]);
           opaque(yr[k]);
           float x[EPV], w[EPV];
@@ -541,7 +670,7 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
           const int vi = tv + k * kThreads;
 #pragma unroll
           for (int e = 0; e < EPV; ++e) {
-            const bool valid = (vi < cv1) && (vi * EPV + e < P.vocab);
+            const bool valid = slowv[k] && (vi < cv1) && (vi * EPV + e < P.vocab);
             const float p = rc.p(x[e]);
             const float t = p * ((x[e] - w[e]) - delta);
             const bool clipped = t > tau;
@@ -551,14 +680,8 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
           fence_vals(r_slow, s_slow);
         }
       }
-      float s_c = __builtin_fmaf(scale, s_fast, s_slow);
-      float r_c = __builtin_fmaf(scale, r_fast, r_slow);
-      s_c = wave_sum(s_c);
-      r_c = wave_sum(r_c);
-      if (lane == 0) {
-        sh.red[wave][6] = s_c;
-        sh.red[wave][7] = r_c;
-      }
+      put4(sh, 6, wsum(s_fast + s_slow));
+      put4(sh, 7, wsum(r_fast + r_slow));
       __syncthreads();
       if (tid == 0) {
         sh.out[0] = (sh.red[0][6] + sh.red[1][6]) + (sh.red[2][6] + sh.red[3][6]);
@@ -570,10 +693,14 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
       if (P.G > 1) {
         if (!exchange<kStage2Units>(sh, P, team, chunk, 1, flag1 + 1u, need_rx2)) break;
         if (need_rx2) {
-          for (int c = 0; c < P.G; ++c) {
-            S += __uint_as_float(sh.rx[c * kStage2Units + 0]);
-            rkl += __uint_as_float(sh.rx[c * kStage2Units + 1]);
+          const int lane = tid & 63;
+          float ls = 0.f, lr = 0.f;
+          for (int c = lane; c < P.G; c += 64) {
+            ls += __uint_as_float(sh.rx[c * kStage2Units + 0]);
+            lr += __uint_as_float(sh.rx[c * kStage2Units + 1]);
           }
+          S = wsum(ls);
+          rkl = wsum(lr);
         }
       } else {
         S = sh.out[0];
@@ -596,45 +723,42 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
       }
 
       if constexpr (MODE == kFused) {
-        // ---- phase C: dz (coefficients shared with k_bwd)
-        const float wrow = P.grad_loss ? P.grad_loss[row] : 1.f;
-        const float wa = wrow * alpha;
-        const float k0 = wrow * (alpha * (one_m_delta - S) + (1.f - alpha));
-        const float kc = wrow * ((1.f - alpha) - alpha * S);
-        const float wce = wrow * (1.f - alpha);
+        // ---- phase C: dz (formulas shared with k_bwd through dz_vector)
+        DzConst dc;
+        dc.init(rc, S, alpha, P.grad_loss ? P.grad_loss[row] : 1.f);
         uint8_t* drow = P.dz + (int64_t)row * P.ld_dz_bytes;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
+          opaque(zr[k]);
+          opaque(yr[k]);
+          float x[EPV], w[EPV], o[EPV];
+          In::decode(zr[k], x);
+          In::decode(yr[k], w);
+          dz_vector<EPV>(x, w, slowv[k], __builtin_amdgcn_ballot_w64(slowv[k]) != 0, rc, dc, tau, o);
           const int vi = tv + k * kThreads;
-          if (vi < cv1) {
-            opaque(zr[k]);
-            opaque(yr[k]);
-            float x[EPV], w[EPV], o[EPV];
-            In::decode(zr[k], x);
-            In::decode(yr[k], w);
-            const bool slow = rc.p(zmv[k]) * fmaxf(dmv[k] - delta, 0.f) > tau;
+          const int g0 = vi * EPV;
+          fix_target<EPV>(o, g0, atop, dc.wce);
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-              const float p = rc.p(x[e]);
-              const float d = x[e] - w[e];
-              float coef = __builtin_fmaf(wa, d, k0);
-              if (slow) coef = (p * (d - delta) > tau) ? kc : coef;
-              o[e] = p * coef;
-            }
-            const int g0 = vi * EPV;
-            if (atop >= g0 && atop < g0 + EPV) {
-#pragma unroll
-              for (int e = 0; e < EPV; ++e) o[e] = (g0 + e == atop) ? o[e] - wce : o[e];
-            }
-            uint8_t* dst = drow + (int64_t)g0 * OSZ;
-#pragma unroll
-            for (int e = 0; e < EPV; e += 4) fence_vals(o[e], o[e + 1], o[e + 2], o[e + 3]);
+          for (int e = 0; e < EPV; e += 4) fence_vals(o[e], o[e + 1], o[e + 2], o[e + 3]);
+          uint8_t* dst = drow + (int64_t)g0 * OSZ;
+          if ((k + 1) * kThreads <= clen && !tail_chunk) {  // uniform: every lane holds a full vector
+            store_vec<OutBF16, EPV>(dst, o);
+          } else if (vi < cv1) {
             if (g0 + EPV <= P.vocab) {
               store_vec<OutBF16, EPV>(dst, o);
             } else {
               store_partial<OutBF16, EPV>(dst, o, P.vocab - g0);
             }
           }
+        }
+      }
+    }
+    if constexpr (PF) {
+      if (next_row < P.n_rows) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          zr[k] = nz[k];
+          yr[k] = ny[k];
         }
       }
     }
@@ -652,17 +776,12 @@ __global__ void __launch_bounds__(kThreads) k_bwd(BwdParams P) {
   constexpr int OSZ = OutBF16 ? 2 : 4;
   const int row = blockIdx.y;
   const float* st = P.row_stats + 8 * (int64_t)row;
-  const float S = st[2];
   RowConst rc;
   rc.init(st[4], st[5], st[6]);
-  const float delta = rc.delta;
+  DzConst dc;
+  dc.init(rc, st[2], P.alpha, P.grad_loss ? P.grad_loss[row] : 1.f);
   const int atop = P.target_top1[row];
-  const float alpha = P.alpha, tau = P.tau;
-  const float wrow = P.grad_loss ? P.grad_loss[row] : 1.f;
-  const float wa = wrow * alpha;
-  const float k0 = wrow * (alpha * ((1.f - delta) - S) + (1.f - alpha));
-  const float kc = wrow * ((1.f - alpha) - alpha * S);
-  const float wce = wrow * (1.f - alpha);
+  const float tau = P.tau;
   const uint4* zrow = (const uint4*)(P.z + (int64_t)row * P.ld_bytes);
   const uint4* yrow = (const uint4*)(P.y + (int64_t)row * P.ld_bytes);
   uint8_t* drow = P.dz + (int64_t)row * P.ld_dz_bytes;
@@ -671,8 +790,8 @@ __global__ void __launch_bounds__(kThreads) k_bwd(BwdParams P) {
 #pragma unroll
   for (int k = 0; k < kBwdVecPerThread; ++k) {
     const int vc = min(v0 + k * kThreads, P.nvec - 1);
-    zr[k] = zrow[vc];
-    yr[k] = yrow[vc];
+    zr[k] = load_nt(zrow + vc);
+    yr[k] = load_nt(yrow + vc);
   }
 #pragma unroll
   for (int k = 0; k < kBwdVecPerThread; ++k) {
@@ -692,31 +811,21 @@ __global__ void __launch_bounds__(kThreads) k_bwd(BwdParams P) {
 #pragma unroll
   for (int k = 0; k < kBwdVecPerThread; ++k) {
     const int vi = v0 + k * kThreads;
+    float x[EPV], w[EPV], o[EPV];
+    In::decode(zr[k], x);
+    In::decode(yr[k], w);
+    // the fused kernel's vector bound, recomputed: same decisions, bit-identical dz
+    float zm = x[0], dm = x[0] - w[0];
+#pragma unroll
+    for (int e = 1; e < EPV; ++e) {
+      zm = fmaxf(zm, x[e]);
+      dm = fmaxf(dm, x[e] - w[e]);
+    }
+    const bool slow = rc.p(zm) * fmaxf(dm - rc.delta, 0.f) > tau;
+    dz_vector<EPV>(x, w, slow, __builtin_amdgcn_ballot_w64(slow) != 0, rc, dc, tau, o);
+    const int g0 = vi * EPV;
+    fix_target<EPV>(o, g0, atop, dc.wce);
     if (vi < P.nvec) {
-      float x[EPV], w[EPV], o[EPV];
-      In::decode(zr[k], x);
-      In::decode(yr[k], w);
-      // the fused kernel's vector bound, recomputed: same decisions, bit-identical dz
-      float zm = x[0], dm = x[0] - w[0];
-#pragma unroll
-      for (int e = 1; e < EPV; ++e) {
-        zm = fmaxf(zm, x[e]);
-        dm = fmaxf(dm, x[e] - w[e]);
-      }
-      const bool slow = rc.p(zm) * fmaxf(dm - delta, 0.f) > tau;
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float p = rc.p(x[e]);
-        const float d = x[e] - w[e];
-        float coef = __builtin_fmaf(wa, d, k0);
-        if (slow) coef = (p * (d - delta) > tau) ? kc : coef;
-        o[e] = p * coef;
-      }
-      const int g0 = vi * EPV;
-      if (atop >= g0 && atop < g0 + EPV) {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) o[e] = (g0 + e == atop) ? o[e] - wce : o[e];
-      }
       uint8_t* dst = drow + (int64_t)g0 * OSZ;
       if (g0 + EPV <= P.vocab) {
         store_vec<OutBF16, EPV>(dst, o);
@@ -758,22 +867,23 @@ __global__ void k_fill_u32(uint32_t* dst, uint32_t value, size_t count) {
 
 // ---------------------------------------------------------------- instantiation tables
 
-template <int MODE>
+template <int MODE, bool PF>
 void* team_kernel(int in_bf16, int out_bf16, int K) {
   if (MODE != kFused) out_bf16 = 0;
   if (in_bf16) {
-    if (out_bf16) return K == 1 ? (void*)k_team<BF16In, true, 1, MODE> : (void*)k_team<BF16In, true, 5, MODE>;
-    return K == 1 ? (void*)k_team<BF16In, false, 1, MODE> : (void*)k_team<BF16In, false, 5, MODE>;
+    if (out_bf16) return K == 1 ? (void*)k_team<BF16In, true, 1, MODE, PF> : (void*)k_team<BF16In, true, 5, MODE, PF>;
+    return K == 1 ? (void*)k_team<BF16In, false, 1, MODE, PF> : (void*)k_team<BF16In, false, 5, MODE, PF>;
   }
-  if (out_bf16) return K == 1 ? (void*)k_team<F32In, true, 1, MODE> : (void*)k_team<F32In, true, 5, MODE>;
-  return K == 1 ? (void*)k_team<F32In, false, 1, MODE> : (void*)k_team<F32In, false, 5, MODE>;
+  if (out_bf16) return K == 1 ? (void*)k_team<F32In, true, 1, MODE, PF> : (void*)k_team<F32In, true, 5, MODE, PF>;
+  return K == 1 ? (void*)k_team<F32In, false, 1, MODE, PF> : (void*)k_team<F32In, false, 5, MODE, PF>;
 }
 
 void* team_kernel_any(int mode, int in_bf16, int out_bf16, int K) {
   switch (mode) {
-    case kFused: return team_kernel<kFused>(in_bf16, out_bf16, K);
-    case kForward: return team_kernel<kForward>(in_bf16, out_bf16, K);
-    default: return team_kernel<kTop1>(in_bf16, out_bf16, K);
+    case kFused: return kPrefetchRows ? team_kernel<kFused, true>(in_bf16, out_bf16, K)
+                                      : team_kernel<kFused, false>(in_bf16, out_bf16, K);
+    case kForward: return team_kernel<kForward, false>(in_bf16, out_bf16, K);
+    default: return team_kernel<kTop1, false>(in_bf16, out_bf16, K);
   }
 }
 
