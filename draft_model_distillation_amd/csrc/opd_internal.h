@@ -24,9 +24,6 @@ constexpr uint32_t kFlagBadOffsets = 2u;
 constexpr uint32_t kFlagSpinTimeout = 4u;
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 constexpr int kMaxTeamSize = 128;
-// Fused kernel keeps the next row's chunk in flight in a second register buffer (3 instead of 4
-// workgroups per CU). Chosen by measurement.
-constexpr bool kPrefetchRows = false;
 
 enum Mode : int { kFused = 0, kForward = 1, kTop1 = 2 };
 

@@ -160,36 +160,6 @@ __device__ __forceinline__ void store_partial(uint8_t* dst, const float (&o)[EPV
   }
 }
 
-// ---------------------------------------------------------------- wave / block reductions
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
-}
-// (index, value) pair: smaller index wins
-__device__ __forceinline__ void wave_min_pair(int& i, float& v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    int oi = __shfl_xor(i, o);
-    float ov = __shfl_xor(v, o);
-    if (oi < i) {
-      i = oi;
-      v = ov;
-    }
-  }
-}
-
 // ---------------------------------------------------------------- cross-workgroup exchange
 
 __device__ __forceinline__ void unit_store(uint64_t* p, uint32_t flag, uint32_t bits) {
@@ -367,21 +337,6 @@ __device__ __forceinline__ void fence_vals(float& a, float& b, float& c, float& 
   __asm__ volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
-// Requests this thread's K vectors of a row's chunk of z and y (nontemporal, indices clamped into
-// the chunk so that every lane loads valid memory and no branch separates the loads).
-template <int K>
-__device__ __forceinline__ void load_chunk(uint4 (&zr)[K], uint4 (&yr)[K], const TeamParams& P, int row, int tv,
-                                           int cv1) {
-  const uint4* zrow = (const uint4*)(P.z + (int64_t)row * P.ld_bytes);
-  const uint4* yrow = (const uint4*)(P.y + (int64_t)row * P.ld_bytes);
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int vc = min(tv + k * kThreads, cv1 - 1);
-    zr[k] = load_nt(zrow + vc);
-    yr[k] = load_nt(yrow + vc);
-  }
-}
-
 // Workgroup-wide combine of wave-uniform values through LDS (4 waves).
 __device__ __forceinline__ void put4(Shared& sh, int slot, float v) {
   if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6][slot] = v;
@@ -389,11 +344,15 @@ __device__ __forceinline__ void put4(Shared& sh, int slot, float v) {
 
 // ---------------------------------------------------------------- the row-team kernel
 
-template <class In, bool OutBF16, int K, int MODE, bool PF>
-__global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
+template <class In, bool OutBF16, int K, int MODE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) k_team(TeamParams P) {
   constexpr int EPV = In::EPV;
   constexpr int OSZ = OutBF16 ? 2 : 4;
   __shared__ Shared sh;
+  // The row chunk of y lives in LDS (written by direct global->LDS loads), z in VGPRs: this keeps
+  // the register footprint within 5 workgroups per CU (the occupancy the kernel is built for, as
+  // more resident teams hide the exchange waits). Each lane only ever reads back its own 16 bytes.
+  __shared__ uint4 ylds[K * kThreads];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   int team, chunk;
@@ -412,14 +371,7 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
   const bool tail_chunk = (cv1 == P.nvec) && (P.nvec * EPV != P.vocab);
   if (tid == 0) sh.err = 0;
 
-  // Rows may be double-buffered in registers (PF): the next row's chunk is then requested at the
-  // top of each row pass so that its latency overlaps this row's work.
-  uint4 zr[K], yr[K];
-  if constexpr (PF) {
-    int tv = cv0 + tid;
-    __asm__ volatile("" : "+v"(tv));
-    if (team < P.n_rows) load_chunk<K>(zr, yr, P, team, tv, cv1);
-  }
+  uint4 zr[K];
   int iter = 0;
   for (int row = team; row < P.n_rows; row += P.n_teams, ++iter) {
     __syncthreads();
@@ -427,24 +379,32 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
     // index and bounds test out of the row loop and keeps them all in registers.
     int tv = cv0 + tid;
     __asm__ volatile("" : "+v"(tv));
-    const int next_row = row + P.n_teams;
-    uint4 nz[K], ny[K];
-    if constexpr (PF) {
-      if (next_row < P.n_rows) load_chunk<K>(nz, ny, P, next_row, tv, cv1);
-    } else {
-      load_chunk<K>(zr, yr, P, row, tv, cv1);
+    {
+      // All loads of the chunk are issued back to back (indices clamped into the chunk: no branch,
+      // no wait between them): z into VGPRs, y straight into this lane's LDS slots.
+      const uint4* zrow = (const uint4*)(P.z + (int64_t)row * P.ld_bytes);
+      const uint4* yrow = (const uint4*)(P.y + (int64_t)row * P.ld_bytes);
+      const int wbase = (tid >> 6) << 6;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int vc = min(tv + k * kThreads, cv1 - 1);
+        zr[k] = load_nt(zrow + vc);
+        __builtin_amdgcn_global_load_lds(yrow + vc, (__attribute__((address_space(3))) void*)(ylds + k * kThreads + wbase),
+                                         16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {  // the current row must be in registers from here on
       opaque(zr[k]);
-      opaque(yr[k]);
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       if ((k + 1) * kThreads > clen) {  // uniform: only slots that can run past the chunk end
-        const bool in = tv + k * kThreads < cv1;
-        zr[k] = in ? zr[k] : splat4(In::kSentinel);
-        yr[k] = in ? yr[k] : splat4(In::kSentinel);
+        if (tv + k * kThreads >= cv1) {
+          zr[k] = splat4(In::kSentinel);
+          ylds[k * kThreads + tid] = splat4(In::kSentinel);
+        }
       }
     }
     if (tail_chunk) {  // uniform: only the chunk holding a partial last vector
@@ -452,8 +412,10 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
       for (int k = 0; k < K; ++k) {
         const int vi = tv + k * kThreads;
         if (vi == P.nvec - 1) {
+          uint4 yv = ylds[k * kThreads + tid];
           mask_tail<In>(zr[k], P.vocab - vi * EPV);
-          mask_tail<In>(yr[k], P.vocab - vi * EPV);
+          mask_tail<In>(yv, P.vocab - vi * EPV);
+          ylds[k * kThreads + tid] = yv;
         }
       }
     }
@@ -468,10 +430,9 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       opaque(zr[k]);
-      opaque(yr[k]);
       float x[EPV], w[EPV];
       In::decode(zr[k], x);
-      In::decode(yr[k], w);
+      In::decode(ylds[k * kThreads + tid], w);
       float zm = x[0], ym = w[0], dm = x[0] - w[0];
 #pragma unroll
       for (int e = 1; e < EPV; ++e) {
@@ -536,10 +497,9 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
 #pragma unroll
       for (int k = K - 1; k >= 0; --k) {
         opaque(zr[k]);
-        opaque(yr[k]);
         float x[EPV], w[EPV];
         In::decode(zr[k], x);
-        In::decode(yr[k], w);
+        In::decode(ylds[k * kThreads + tid], w);
 #pragma unroll
         for (int e = EPV - 1; e >= 0; --e) {
           const bool hit = (w[e] == m_y);
@@ -663,10 +623,9 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
         r_fast += slowv[k] ? 0.f : scale * __builtin_fmaf(-delta, ek[k], bk[k]);
         if (__builtin_amdgcn_ballot_w64(slowv[k])) {
           opaque(zr[k]);
-          opaque(yr[k]);
           float x[EPV], w[EPV];
           In::decode(zr[k], x);
-          In::decode(yr[k], w);
+          In::decode(ylds[k * kThreads + tid], w);
           const int vi = tv + k * kThreads;
 #pragma unroll
           for (int e = 0; e < EPV; ++e) {
@@ -730,10 +689,9 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
           opaque(zr[k]);
-          opaque(yr[k]);
           float x[EPV], w[EPV], o[EPV];
           In::decode(zr[k], x);
-          In::decode(yr[k], w);
+          In::decode(ylds[k * kThreads + tid], w);
           dz_vector<EPV>(x, w, slowv[k], __builtin_amdgcn_ballot_w64(slowv[k]) != 0, rc, dc, tau, o);
           const int vi = tv + k * kThreads;
           const int g0 = vi * EPV;
@@ -750,15 +708,6 @@ __global__ void __launch_bounds__(kThreads) k_team(TeamParams P) {
               store_partial<OutBF16, EPV>(dst, o, P.vocab - g0);
             }
           }
-        }
-      }
-    }
-    if constexpr (PF) {
-      if (next_row < P.n_rows) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          zr[k] = nz[k];
-          yr[k] = ny[k];
         }
       }
     }
@@ -867,23 +816,22 @@ __global__ void k_fill_u32(uint32_t* dst, uint32_t value, size_t count) {
 
 // ---------------------------------------------------------------- instantiation tables
 
-template <int MODE, bool PF>
+template <int MODE>
 void* team_kernel(int in_bf16, int out_bf16, int K) {
   if (MODE != kFused) out_bf16 = 0;
   if (in_bf16) {
-    if (out_bf16) return K == 1 ? (void*)k_team<BF16In, true, 1, MODE, PF> : (void*)k_team<BF16In, true, 5, MODE, PF>;
-    return K == 1 ? (void*)k_team<BF16In, false, 1, MODE, PF> : (void*)k_team<BF16In, false, 5, MODE, PF>;
+    if (out_bf16) return K == 1 ? (void*)k_team<BF16In, true, 1, MODE> : (void*)k_team<BF16In, true, 5, MODE>;
+    return K == 1 ? (void*)k_team<BF16In, false, 1, MODE> : (void*)k_team<BF16In, false, 5, MODE>;
   }
-  if (out_bf16) return K == 1 ? (void*)k_team<F32In, true, 1, MODE, PF> : (void*)k_team<F32In, true, 5, MODE, PF>;
-  return K == 1 ? (void*)k_team<F32In, false, 1, MODE, PF> : (void*)k_team<F32In, false, 5, MODE, PF>;
+  if (out_bf16) return K == 1 ? (void*)k_team<F32In, true, 1, MODE> : (void*)k_team<F32In, true, 5, MODE>;
+  return K == 1 ? (void*)k_team<F32In, false, 1, MODE> : (void*)k_team<F32In, false, 5, MODE>;
 }
 
 void* team_kernel_any(int mode, int in_bf16, int out_bf16, int K) {
   switch (mode) {
-    case kFused: return kPrefetchRows ? team_kernel<kFused, true>(in_bf16, out_bf16, K)
-                                      : team_kernel<kFused, false>(in_bf16, out_bf16, K);
-    case kForward: return team_kernel<kForward, false>(in_bf16, out_bf16, K);
-    default: return team_kernel<kTop1, false>(in_bf16, out_bf16, K);
+    case kFused: return team_kernel<kFused>(in_bf16, out_bf16, K);
+    case kForward: return team_kernel<kForward>(in_bf16, out_bf16, K);
+    default: return team_kernel<kTop1>(in_bf16, out_bf16, K);
   }
 }
 
