@@ -19,6 +19,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libopd_mi355x.so"
 SOURCES = ["opd_kernels.hip", "opd_api.cpp"]
+# Kernels only: the VALU runs with the IEEE mode bit clear, so max/min need no NaN-quieting
+# canonicalisation of their operands (inputs are finite by contract). The host file keeps IEEE NaN
+# semantics for its argument checks.
+KERNEL_ONLY = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
 
 COMMON = [
     "--offload-arch=gfx950",
@@ -52,7 +56,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        lang = ["-x", "hip", *KERNEL_ONLY] if src.endswith(".hip") else []
         cmd = [cc, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -10,24 +10,29 @@
 //    a drafted block within the predicted verification length L.
 //  - same article, section "Infrastructure: ... Variable-Length Batching": packed ragged blocks.
 //
-// Design (MI355X): the path is HBM-bound streaming (no dense contraction, so no MFMA). A 151,936-wide
-// bf16 row is 297 KiB per tensor, more than one CU can hold, so a row is split over a *team* of G
-// workgroups. Each workgroup keeps its chunk of z and y in VGPRs (packed bf16) for the whole row:
-//   phase A  chunk max, sum-exp of z and y, per-vector sums of e^(z_v - m) and e^(z_v - m)(z_v - y_v),
-//            first argmax of z and y
-//   -- exchange 1 --  every member combines the G partials in the same fixed order
-//   phase B  S and the clipped reverse KL: vectors whose bound max(p) * max(z - y - delta, 0) is
-//            <= tau provably hold no clipped term and use their phase-A sums; the rest are visited
-//            element by element
-//   -- exchange 2 --
+// Design (MI355X): a streaming reduction, no dense contraction (so no MFMA). A 151,936-wide bf16 row
+// is 297 KiB per tensor, more than one CU can hold, so a row is split over a *team* of G workgroups;
+// each keeps its chunk resident for the whole row (z packed in VGPRs, y in LDS through direct
+// buffer-to-LDS loads), so z and y are read from HBM once and dz written once:
+//   phase A  per 16-byte vector: max z, max y, max(z - y), and sums of 2^(z log2e - c) and of the
+//            same terms times (z - y) relative to the vector's own c = fl(max z log2e); one running
+//            sum of 2^(y log2e - r) per lane
+//   chunk    maxima, lowest indices of the maxima, sums rescaled to the chunk maxima
+//   -- exchange 1 --  wave 0 publishes 7 values, gathers all members' and combines them in a fixed
+//                     order: every member derives identical row constants
+//   phase B  S and the clipped reverse KL: vectors whose bound is <= tau provably hold no clipped
+//            term and use their phase-A sums; the rest (near the peak) are visited element by element
+//   -- exchange 2 --  the two sums
 //   phase C  dz written once (bf16 rounded to nearest even, or fp32)
-// so z and y are read from HBM once and dz written once. Exchanges use 8-byte [value | flag] units
-// written and polled with agent-scope relaxed atomics (sc1: coherent across XCDs without L2
-// writeback / invalidate); the flag is unique per launch, row iteration and stage, so nothing has to
-// be reset between launches and a stale unit can never be taken for a fresh one. Every wait is
-// bounded and raises a sticky flag instead of hanging. Team members are mapped to one XCD when the
-// team count allows (workgroups are dispatched round-robin over the 8 XCDs).
-//
+// The kernel is VALU-heavy for an HBM stream (about 30 lane-ops and 3.5 exponentials per element),
+// so the per-element work is kept minimal and the per-row work (reductions, exchanges, row
+// constants) runs once per workgroup in wave 0 while the other waves wait at barriers and the SIMDs
+// serve the other resident workgroups. Exchanges use 8-byte [value | flag] units written and
+// polled with agent-scope relaxed atomics (sc1: coherent across XCDs without L2 writeback /
+// invalidate); the flag is unique per launch, row iteration and stage, so nothing has to be reset
+// between launches and a stale unit can never be taken for a fresh one. Every wait is bounded and
+// raises a sticky flag instead of hanging.
+
 // Numerics: fp32 throughout with fixed reduction orders (bitwise deterministic). Per row, with
 // M = max z, S_z = sum_v e^(z_v - M), delta = LSE(z) - LSE(y), t_v = p_v (z_v - y_v - delta):
 //   clipped reverse KL = sum_v min(t_v, tau),  S = sum_v [t_v <= tau] p_v (t_v / p_v + 1),
@@ -49,10 +54,18 @@ namespace opd {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kBig = 0x7fffffff;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }  // v_log_f32, normal x
+
+// Work-item and workgroup ids straight from the hardware registers. The kernels are built with the
+// IEEE mode bit clear, which the device library is not: its id helpers would not be inlined.
+__device__ __forceinline__ int thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int block_id_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int block_id_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
 
 // ---------------------------------------------------------------- input formats (16-byte vectors)
 
@@ -160,18 +173,70 @@ __device__ __forceinline__ void store_partial(uint8_t* dst, const float (&o)[EPV
   }
 }
 
+// ---------------------------------------------------------------- buffer access
+
+// Raw buffer resources (gfx9 descriptor word 3: 32-bit data format, no swizzle). Loads past
+// num_records return 0 and stores past it are dropped, so the lanes of a slot that runs past the
+// end of a chunk need neither a clamped address nor a branch.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kNT = 2;  // cache policy: nontemporal (the logits are read once, dz written once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, int off, uint32_t a, uint32_t b, uint32_t c,
+                                            uint32_t d) {
+  const u32x4 v = {a, b, c, d};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNT);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, uint32_t a, uint32_t b) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = {a, b};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kNT);
+}
+// 16 bytes per lane straight into LDS: lane i of the wave lands at wave_base + 16 i.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, int off, uint4* wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)wave_base, 16, off, 0, 0, kNT);
+}
+
+// dz of one 16-byte input vector (EPV values) through a buffer resource; `off` is the vector's byte
+// offset in the output (EPV * OSZ bytes per vector).
+template <bool OutBF16, int EPV>
+__device__ __forceinline__ void buf_store_vec(__amdgpu_buffer_rsrc_t r, int off, const float (&o)[EPV]) {
+  if constexpr (OutBF16) {
+    if constexpr (EPV == 8) {
+      buf_store16(r, off, pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7]));
+    } else {
+      buf_store8(r, off, pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < EPV / 4; ++q) {
+      buf_store16(r, off + 16 * q, __float_as_uint(o[4 * q]), __float_as_uint(o[4 * q + 1]),
+                  __float_as_uint(o[4 * q + 2]), __float_as_uint(o[4 * q + 3]));
+    }
+  }
+}
+
 // ---------------------------------------------------------------- cross-workgroup exchange
 
 __device__ __forceinline__ void unit_store(uint64_t* p, uint32_t flag, uint32_t bits) {
   uint64_t u = ((uint64_t)flag << 32) | (uint64_t)bits;
   __hip_atomic_store(p, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t unit_load(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-// Poll one unit until its flag matches; returns false when the bound was exceeded.
+// Polls one unit until it carries `flag`; returns false when the bound on polls was exceeded.
 __device__ __forceinline__ bool unit_wait(const uint64_t* p, uint32_t flag, uint32_t limit, uint32_t& bits) {
   uint32_t spins = 0;
   while (true) {
-    uint64_t u = __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t u = unit_load(p);
     if ((uint32_t)(u >> 32) == flag) {
       bits = (uint32_t)u;
       return true;
@@ -181,37 +246,63 @@ __device__ __forceinline__ bool unit_wait(const uint64_t* p, uint32_t flag, uint
   }
 }
 
+// Wave 0 alone gathers the NU values of all G members into rx[c * NU + j]: each lane polls units
+// ln, ln + 64, ... two at a time (both loads in flight together). Returns false (wave-uniformly) when
+// a wait exceeded its bound.
+template <int NU>
+__device__ __forceinline__ bool gather_wave(uint32_t* rx, const uint64_t* units, int G, int ln, uint32_t flag,
+                                            uint32_t limit) {
+  const int n = G * NU;
+  bool ok = true;
+  for (int base = 0; base < n; base += 128) {
+    const int i0 = base + ln, i1 = base + 64 + ln;
+    bool d0 = i0 >= n, d1 = i1 >= n;
+    const uint64_t* p0 = units + (size_t)(i0 / NU) * 8 + i0 % NU;
+    const uint64_t* p1 = units + (size_t)(i1 / NU) * 8 + i1 % NU;
+    uint32_t spins = 0;
+    while (!(d0 && d1)) {
+      const uint64_t u0 = d0 ? 0 : unit_load(p0);
+      const uint64_t u1 = d1 ? 0 : unit_load(p1);
+      if (!d0 && (uint32_t)(u0 >> 32) == flag) {
+        rx[i0] = (uint32_t)u0;
+        d0 = true;
+      }
+      if (!d1 && (uint32_t)(u1 >> 32) == flag) {
+        rx[i1] = (uint32_t)u1;
+        d1 = true;
+      }
+      if (d0 && d1) break;
+      if (++spins > limit) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  return __builtin_amdgcn_ballot_w64(!ok) == 0;
+}
+
+// Wave 0 of every member publishes this chunk's NU values from LDS (lanes 0..NU-1, one unit each).
+template <int NU>
+__device__ __forceinline__ void publish(uint64_t* units, int lane, uint32_t flag, const uint32_t* vals) {
+  if (lane < NU) unit_store(units + lane, flag, vals[lane]);
+}
+
+// LDS shared by the waves of a workgroup (the chunk of y lives in its own array).
 struct Shared {
-  float red[4][8];
-  int ired[4][4];
-  float out[8];
-  uint32_t rx[128 * kStage1Units];
+  uint32_t rx[kMaxTeamSize * kStage1Units];  // gathered member values (wave 0)
+  uint32_t part[8];  // this chunk's values to publish
+  float wred[4][4];  // per-wave partials
+  int widx[4][2];    // per-wave first argmax of z and y
+  float wza[4];      // z at the wave's argmax of y
+  float row[12];     // row constants, written by wave 0
   int err;
 };
 
-// Publish NU values of this chunk and gather every chunk's values into sh.rx[c * NU + j].
-// Returns false (uniformly over the workgroup) if a wait exceeded its bound.
-template <int NU>
-__device__ __forceinline__ bool exchange(Shared& sh, const TeamParams& P, int team, int chunk, int stage,
-                                         uint32_t flag, bool receive) {
-  uint64_t* base = P.units + ((size_t)team * 2 + stage) * (size_t)P.G * 8;
-  const int tid = threadIdx.x;
-  if (tid < NU) {
-    unit_store(base + (size_t)chunk * 8 + tid, flag, __float_as_uint(sh.out[tid]));
-  }
-  if (receive) {
-    bool ok = true;
-    for (int i = tid; i < P.G * NU; i += kThreads) {
-      uint32_t bits = 0;
-      const int c = i / NU, j = i - c * NU;
-      if (!unit_wait(base + (size_t)c * 8 + j, flag, P.spin_limit, bits)) ok = false;
-      sh.rx[i] = bits;
-    }
-    if (!ok) sh.err = 1;
-  }
-  __syncthreads();
-  return sh.err == 0;
-}
+// Row constants in Shared::row.
+enum RowSlot : int {
+  kRowMz = 0, kRowLnSz, kRowDelta, kRowMy, kRowLnSy, kRowDtop, kRowAtop, kRowZa, kRowS, kRowRkl
+};
 
 // ---------------------------------------------------------------- wave reductions (DPP)
 
@@ -244,9 +335,11 @@ __device__ __forceinline__ int dppi(int v, int id, int which) {
 __device__ __forceinline__ float uniform_f(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// max and min are idempotent: lanes a broadcast step leaves out may keep their own value as the
+// "old" operand, which saves the identity move of every step.
 __device__ __forceinline__ float wmax(float v) {
 #pragma unroll
-  for (int s = 0; s < 6; ++s) v = fmaxf(v, dppf(v, kNegInf, s));
+  for (int s = 0; s < 6; ++s) v = fmaxf(v, dppf(v, v, s));
   return uniform_f(v);
 }
 __device__ __forceinline__ float wsum(float v) {
@@ -256,7 +349,7 @@ __device__ __forceinline__ float wsum(float v) {
 }
 __device__ __forceinline__ int wmin(int v) {
 #pragma unroll
-  for (int s = 0; s < 6; ++s) v = min(v, dppi(v, kBig, s));
+  for (int s = 0; s < 6; ++s) v = min(v, dppi(v, v, s));
   return __builtin_amdgcn_readlane(v, 63);
 }
 
@@ -297,6 +390,19 @@ struct DzConst {
   }
 };
 
+// Vector bound of phase B: every term t_v = p(x_v) ((x_v - y_v) - delta) of a 16-byte vector is at
+// most p(max x) max(max(x - y) - delta, 0). p(max x) is replaced by sc = 2^(fl(max x log2 e) - c_hi -
+// c_lo), the factor that also scales the vector's phase-A sums; the two differ by a factor below
+// 1.003 for |x| <= 1e4, so the test runs against tau / 1.01: a vector that passes holds no term above
+// tau. The same test, from the same floats, runs in the fused and the backward kernels.
+constexpr float kBoundShrink = 1.f / 1.01f;
+__device__ __forceinline__ float vector_scale(const RowConst& rc, float zmax) {
+  return exp2_fast((zmax * kLog2e - rc.c_hi) - rc.c_lo);
+}
+__device__ __forceinline__ bool vector_may_clip(const RowConst& rc, float sc, float dmax, float tau_b) {
+  return sc * fmaxf(dmax - rc.delta, 0.f) > tau_b;
+}
+
 // dz of one 16-byte vector. `slow` marks a lane whose vector may hold clipped terms (its bound
 // exceeds tau); `any_slow` is the wave-uniform OR of it, so the clip tests run only in waves that
 // need them. Shared by the fused and the backward kernels (bit-identical results).
@@ -333,28 +439,99 @@ __device__ __forceinline__ void opaque(uint4& v) {
 // (which keeps every slot's decoded inputs and exponentials live at once).
 __device__ __forceinline__ void fence_vals(float& a) { __asm__ volatile("" : "+v"(a)); }
 __device__ __forceinline__ void fence_vals(float& a, float& b) { __asm__ volatile("" : "+v"(a), "+v"(b)); }
+__device__ __forceinline__ void fence_vals(float& a, float& b, float& c) {
+  __asm__ volatile("" : "+v"(a), "+v"(b), "+v"(c));
+}
 __device__ __forceinline__ void fence_vals(float& a, float& b, float& c, float& d) {
   __asm__ volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
-// Workgroup-wide combine of wave-uniform values through LDS (4 waves).
-__device__ __forceinline__ void put4(Shared& sh, int slot, float v) {
-  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6][slot] = v;
+
+// Per-vector maxima kept from phase A to phase B: max z and max(z - y). For bf16 inputs both fit one
+// register: max z is itself a bf16 value (exact), and max(z - y) is rounded up to bf16, which only
+// loosens the phase-B bound (the backward kernel applies the same rounding, so decisions agree).
+template <int EPV>
+struct VecMax {
+  float zm, dm;
+  __device__ __forceinline__ void set(float z, float d) { zm = z; dm = d; }
+  __device__ __forceinline__ float z() const { return zm; }
+  __device__ __forceinline__ float d() const { return dm; }
+  __device__ __forceinline__ void fence() { __asm__ volatile("" : "+v"(zm), "+v"(dm)); }
+};
+__device__ __forceinline__ uint32_t bf16_bits_up(float d) {  // bits of the least bf16 >= d (finite d)
+  const uint32_t u = __float_as_uint(d);
+  return (int32_t)u >= 0 ? (u + 0xffffu) & 0xffff0000u : u & 0xffff0000u;
+}
+template <>
+struct VecMax<8> {
+  uint32_t pk;  // [max(z - y) rounded up : 16][max z : 16]
+  __device__ __forceinline__ void set(float z, float d) { pk = (__float_as_uint(z) >> 16) | bf16_bits_up(d); }
+  __device__ __forceinline__ float z() const { return __uint_as_float(pk << 16); }
+  __device__ __forceinline__ float d() const { return __uint_as_float(pk & 0xffff0000u); }
+  __device__ __forceinline__ void fence() { __asm__ volatile("" : "+v"(pk)); }
+};
+// The bound's max(z - y) as the fused kernel keeps it (see VecMax).
+template <int EPV>
+__device__ __forceinline__ float kept_dmax(float d) {
+  if constexpr (EPV == 8) return __uint_as_float(bf16_bits_up(d));
+  else return d;
+}
+
+// Sum of the EPV values of a vector in a fixed pairwise order.
+template <int EPV>
+__device__ __forceinline__ float vsum(const float (&v)[EPV]) {
+  if constexpr (EPV == 8) return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+  else return (v[0] + v[1]) + (v[2] + v[3]);
+}
+template <int EPV>
+__device__ __forceinline__ float vmax(const float (&v)[EPV]) {
+  float m = fmaxf(v[0], v[1]);
+#pragma unroll
+  for (int e = 2; e < EPV; ++e) m = fmaxf(m, v[e]);
+  return m;
+}
+// First e with v[e] == m (EPV if none).
+template <int EPV>
+__device__ __forceinline__ int first_eq(const float (&v)[EPV], float m) {
+  int e0 = EPV;
+#pragma unroll
+  for (int e = EPV - 1; e >= 0; --e) e0 = (v[e] == m) ? e : e0;
+  return e0;
 }
 
 // ---------------------------------------------------------------- the row-team kernel
+//
+// A team of G workgroups owns a row; workgroup `chunk` owns vectors [cv0, cv0 + clen) of it, each
+// thread the vectors cv0 + tid + 256 k, k < K. Per row:
+//   load     z chunk into VGPRs (packed), y chunk into LDS (direct buffer-to-LDS loads)
+//   phase A  per vector: max z, max y, max(z - y), E_k = sum 2^(z log2e - c_k), B_k = sum of the same
+//            terms times (z - y), with c_k = fl(max z log2e); per lane: sum of 2^(y log2e - r) with r
+//            the first vector's fl(max y log2e) (recomputed from the lane maximum if y climbs more
+//            than 96 octaves above it)
+//   chunk    maxima -> lowest indices of the maxima, sums rescaled to the chunk maxima
+//   team     wave 0 publishes the chunk's 7 values, gathers the G members' values and forms the row
+//            constants (exchange 1)
+//   phase B  S and the clipped reverse KL (vector bound; element by element near the peak);
+//            wave 0 exchanges the 2 sums (exchange 2) and writes the row outputs (chunk 0)
+//   phase C  dz of every vector of the chunk
+// Waves other than wave 0 wait at the barriers while wave 0 exchanges: the SIMDs run the other
+// resident workgroups meanwhile.
+
+typedef __attribute__((address_space(4))) const TeamParams KParams;
 
 template <class In, bool OutBF16, int K, int MODE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) k_team(TeamParams P) {
   constexpr int EPV = In::EPV;
-  constexpr int OSZ = OutBF16 ? 2 : 4;
+  constexpr int VB = EPV * (OutBF16 ? 2 : 4);  // dz bytes per input vector
+  constexpr bool kSums = MODE != kTop1;
   __shared__ Shared sh;
-  // The row chunk of y lives in LDS (written by direct global->LDS loads), z in VGPRs: this keeps
-  // the register footprint within 5 workgroups per CU (the occupancy the kernel is built for, as
-  // more resident teams hide the exchange waits). Each lane only ever reads back its own 16 bytes.
+  // The row chunk of y lives in LDS, z in VGPRs: this keeps the register footprint within 5
+  // workgroups per CU (more resident teams hide the exchange waits). Each lane only ever reads back
+  // its own 16 bytes.
   __shared__ uint4 ylds[K * kThreads];
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x;
+  const int tid = thread_id();
+  const int wave = tid >> 6;
+  const int b = block_id_x();
   int team, chunk;
   if (P.xcd_map) {
     const int x = b & 7, local = b >> 3;
@@ -364,272 +541,346 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
     team = b / P.G;
     chunk = b % P.G;
   }
+  const int G = P.G;
   const int cv0 = chunk * P.chunk_vec;
-  const int cv1 = min(cv0 + P.chunk_vec, P.nvec);
-  const int clen = cv1 - cv0;  // vectors in this chunk (uniform)
-  const float alpha = P.alpha, tau = P.tau;
-  const bool tail_chunk = (cv1 == P.nvec) && (P.nvec * EPV != P.vocab);
+  const int clen0 = min(P.chunk_vec, P.nvec - cv0);  // vectors in this chunk (uniform)
+  const bool tail_chunk = (cv0 + clen0 == P.nvec) && (P.nvec * EPV != P.vocab);
+  uint64_t* const units1 = P.units + (size_t)team * 2 * G * 8;
+  uint64_t* const units2 = units1 + (size_t)G * 8;
   if (tid == 0) sh.err = 0;
 
-  uint4 zr[K];
   int iter = 0;
   for (int row = team; row < P.n_rows; row += P.n_teams, ++iter) {
-    __syncthreads();
-    // Per-thread vector index, made opaque each row: otherwise the compiler hoists every element's
-    // index and bounds test out of the row loop and keeps them all in registers.
-    int tv = cv0 + tid;
-    __asm__ volatile("" : "+v"(tv));
-    {
-      // All loads of the chunk are issued back to back (indices clamped into the chunk: no branch,
-      // no wait between them): z into VGPRs, y straight into this lane's LDS slots.
-      const uint4* zrow = (const uint4*)(P.z + (int64_t)row * P.ld_bytes);
-      const uint4* yrow = (const uint4*)(P.y + (int64_t)row * P.ld_bytes);
-      const int wbase = (tid >> 6) << 6;
+    __syncthreads();  // the previous row is done with ylds and sh
+    // Kernel arguments are re-read (scalar loads) in every row instead of occupying scalar registers
+    // for the whole loop.
+    KParams* pp = (KParams*)__builtin_amdgcn_kernarg_segment_ptr();
+    __asm__ volatile("" : "+s"(pp));
+    // LDS fields are addressed from an opaque zero that is re-derived every row: one base register
+    // plus instruction offsets, instead of one register per field address held across the loop.
+    int z0 = 0;
+    __asm__ volatile("" : "+v"(z0));
+    // Chunk length made opaque per row: per-slot tests are then evaluated where they are used instead
+    // of being hoisted out of the row loop and kept live in scalar registers.
+    int clen = clen0;
+    __asm__ volatile("" : "+s"(clen));
+    // one buffer resource per tensor and row, bounded by the chunk: lanes of a slot past the chunk
+    // end read 0 (replaced by the sentinel below)
+    const __amdgpu_buffer_rsrc_t rz = rsrc(pp->z + (int64_t)row * pp->ld_bytes + (int64_t)cv0 * 16, clen * 16);
+    const __amdgpu_buffer_rsrc_t ry = rsrc(pp->y + (int64_t)row * pp->ld_bytes + (int64_t)cv0 * 16, clen * 16);
+    // The ln index is made opaque once per row: otherwise the compiler hoists every per-slot and
+    // per-element ln test (sentinels, validity, offsets) out of the row loop and keeps them all
+    // live in registers.
+    int lt = tid;
+    __asm__ volatile("" : "+v"(lt));
+    const int voff = lt * 16;
+    const int ln = lt & 63, wv = lt >> 6;
+    const float alpha = pp->alpha, tau = pp->tau, tau_b = tau * kBoundShrink;
+    uint4 zr[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int vc = min(tv + k * kThreads, cv1 - 1);
-        zr[k] = load_nt(zrow + vc);
-        __builtin_amdgcn_global_load_lds(yrow + vc, (__attribute__((address_space(3))) void*)(ylds + k * kThreads + wbase),
-                                         16, 0, 0);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
+    for (int k = 0; k < K; ++k) {  // every load of the chunk in flight at once
+      zr[k] = buf_load16(rz, voff + k * (16 * kThreads));
+      buf_load16_lds(ry, voff + k * (16 * kThreads), ylds + k * kThreads + wv * 64);
     }
-#pragma unroll
-    for (int k = 0; k < K; ++k) {  // the current row must be in registers from here on
-      opaque(zr[k]);
-    }
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      if ((k + 1) * kThreads > clen) {  // uniform: only slots that can run past the chunk end
-        if (tv + k * kThreads >= cv1) {
+      opaque(zr[k]);
+      if ((k + 1) * kThreads > clen) {  // uniform: only slots that run past the chunk end
+        if (lt + k * kThreads >= clen) {
           zr[k] = splat4(In::kSentinel);
-          ylds[k * kThreads + tid] = splat4(In::kSentinel);
+          ylds[k * kThreads + lt] = splat4(In::kSentinel);
         }
       }
     }
     if (tail_chunk) {  // uniform: only the chunk holding a partial last vector
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const int vi = tv + k * kThreads;
-        if (vi == P.nvec - 1) {
-          uint4 yv = ylds[k * kThreads + tid];
-          mask_tail<In>(zr[k], P.vocab - vi * EPV);
-          mask_tail<In>(yv, P.vocab - vi * EPV);
-          ylds[k * kThreads + tid] = yv;
+        const int vi = cv0 + lt + k * kThreads;
+        if (vi == pp->nvec - 1) {
+          uint4 yv = ylds[k * kThreads + lt];
+          mask_tail<In>(zr[k], pp->vocab - vi * EPV);
+          mask_tail<In>(yv, pp->vocab - vi * EPV);
+          ylds[k * kThreads + lt] = yv;
         }
       }
     }
 
-    // ---- phase A (one pass): per 8-element vector, its z max, y max and max(z - y), and the sums
-    // E_k = sum e^(z - zmax_k), B_k = sum e^(z - zmax_k)(z - y), sum e^(y - ymax_k) relative to that
-    // vector's own maxima (so no workgroup maximum is needed first). Exponents use
-    // c = fl(max log2 e); the rounding of c is undone once per vector when folding into the lane's
-    // running (max, sum) pairs, and phase B rescales E_k, B_k by 2^(c_k - c_row).
-    float zmv[K], dmv[K], ek[K], bk[K];
-    float lzmax = kNegInf, lymax = kNegInf, lsz = 0.f, lsy = 0.f;
+    // ---- phase A
+    VecMax<EPV> vm[K];
+    float ek[K], bk[K];
+    float lymax = kNegInf, sy = 0.f, ref_y = 0.f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       opaque(zr[k]);
-      float x[EPV], w[EPV];
+      float x[EPV], w[EPV], d[EPV];
       In::decode(zr[k], x);
-      In::decode(ylds[k * kThreads + tid], w);
-      float zm = x[0], ym = w[0], dm = x[0] - w[0];
+      In::decode(ylds[k * kThreads + lt], w);
+      const float ym = vmax<EPV>(w);
+      lymax = fmaxf(lymax, ym);
+      if constexpr (kSums) {
+        if (k == 0) ref_y = ym * kLog2e;
+        float s2 = exp2_fast(__builtin_fmaf(w[0], kLog2e, -ref_y));
 #pragma unroll
-      for (int e = 1; e < EPV; ++e) {
-        zm = fmaxf(zm, x[e]);
-        ym = fmaxf(ym, w[e]);
-        dm = fmaxf(dm, x[e] - w[e]);
+        for (int e = 1; e < EPV; ++e) s2 += exp2_fast(__builtin_fmaf(w[e], kLog2e, -ref_y));
+        sy = k == 0 ? s2 : sy + s2;
       }
-      zmv[k] = zm;
-      dmv[k] = dm;
-      if constexpr (MODE != kTop1) {
-        const float cz = zm * kLog2e, cy = ym * kLog2e;
-        float se = 0.f, sb = 0.f, sey = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const float ez = exp2_fast(__builtin_fmaf(x[e], kLog2e, -cz));
+      for (int e = 0; e < EPV; ++e) d[e] = x[e] - w[e];
+      const float zmax = vmax<EPV>(x);
+      vm[k].set(zmax, vmax<EPV>(d));
+      if constexpr (kSums) {
+        const float cz = zmax * kLog2e;
+        float ez = exp2_fast(__builtin_fmaf(x[0], kLog2e, -cz));
+        float se = ez, sb = ez * d[0];
+#pragma unroll
+        for (int e = 1; e < EPV; ++e) {
+          ez = exp2_fast(__builtin_fmaf(x[e], kLog2e, -cz));
           se += ez;
-          sb = __builtin_fmaf(ez, x[e] - w[e], sb);
-          sey += exp2_fast(__builtin_fmaf(w[e], kLog2e, -cy));
+          sb = __builtin_fmaf(ez, d[e], sb);
         }
         ek[k] = se;
         bk[k] = sb;
-        // fold into the lane's (max, sum) pairs; exponent offsets: (max_k - M) log2e - (rounding of c)
-        const float nz = fmaxf(lzmax, zm), ny = fmaxf(lymax, ym);
-        lsz = __builtin_fmaf(lsz, exp2_fast((lzmax - nz) * kLog2e),
-                             se * exp2_fast((zm - nz) * kLog2e - __builtin_fmaf(zm, kLog2e, -cz)));
-        lsy = __builtin_fmaf(lsy, exp2_fast((lymax - ny) * kLog2e),
-                             sey * exp2_fast((ym - ny) * kLog2e - __builtin_fmaf(ym, kLog2e, -cy)));
-        lzmax = nz;
-        lymax = ny;
-        fence_vals(lzmax, lymax, lsz, lsy);
-        fence_vals(zmv[k], dmv[k], ek[k], bk[k]);
-      } else {
-        lzmax = fmaxf(lzmax, zm);
-        lymax = fmaxf(lymax, ym);
-        fence_vals(lzmax, lymax);
+        fence_vals(ek[k], bk[k], sy);
       }
+      vm[k].fence();
+      fence_vals(lymax);
     }
-    put4(sh, 0, wmax(lzmax));
-    put4(sh, 1, wmax(lymax));
-    __syncthreads();
-    const float m_z = fmaxf(fmaxf(sh.red[0][0], sh.red[1][0]), fmaxf(sh.red[2][0], sh.red[3][0]));
-    const float m_y = fmaxf(fmaxf(sh.red[0][1], sh.red[1][1]), fmaxf(sh.red[2][1], sh.red[3][1]));
-
-    // ---- lowest index of each chunk maximum: only lanes holding it scan, from the top down with
-    // selects, so the last hit is the lowest index
-    int iz = kBig, iy = kBig;
-    float zat = 0.f;
-    if (lzmax == m_z) {
-      int code = 0;
+    float lzmax = vm[0].z();
 #pragma unroll
-      for (int k = K - 1; k >= 0; --k) {
-        opaque(zr[k]);
-        float x[EPV];
-        In::decode(zr[k], x);
+    for (int k = 1; k < K; ++k) lzmax = fmaxf(lzmax, vm[k].z());
+    if constexpr (kSums) {
+      // the y sum is relative to the first vector's maximum: redo it from the ln maximum where y
+      // rose so far above it that the terms could approach the fp32 range (rare)
+      const bool redo = lymax * kLog2e - ref_y > 96.f;
+      if (__builtin_amdgcn_ballot_w64(redo)) {
+        if (redo) {
+          ref_y = lymax * kLog2e;
+          sy = 0.f;
 #pragma unroll
-        for (int e = EPV - 1; e >= 0; --e) code = (x[e] == m_z) ? k * EPV + e : code;
-      }
-      iz = (tv + (code / EPV) * kThreads) * EPV + code % EPV;
-    }
-    if (lymax == m_y) {
-      int code = 0;
+          for (int k = 0; k < K; ++k) {
+            float w[EPV], ey[EPV];
+            In::decode(ylds[k * kThreads + lt], w);
 #pragma unroll
-      for (int k = K - 1; k >= 0; --k) {
-        opaque(zr[k]);
-        float x[EPV], w[EPV];
-        In::decode(zr[k], x);
-        In::decode(ylds[k * kThreads + tid], w);
-#pragma unroll
-        for (int e = EPV - 1; e >= 0; --e) {
-          const bool hit = (w[e] == m_y);
-          code = hit ? k * EPV + e : code;
-          zat = hit ? x[e] : zat;
+            for (int e = 0; e < EPV; ++e) ey[e] = exp2_fast(__builtin_fmaf(w[e], kLog2e, -ref_y));
+            sy += vsum<EPV>(ey);
+          }
         }
       }
-      iy = (tv + (code / EPV) * kThreads) * EPV + code % EPV;
     }
+
+    // ---- chunk maxima
     {
-      const int wiz = wmin(iz);
-      const int wiy = wmin(iy);
-      const float wza = wsum(iy == wiy ? zat : 0.f);  // the lane that owns the index (unique)
-      if constexpr (MODE != kTop1) {
-        // chunk sums relative to the chunk maxima (lane pairs rescaled exactly: bf16/fp32 maxima)
-        put4(sh, 2, wsum(lsz * exp2_fast((lzmax - m_z) * kLog2e)));
-        put4(sh, 3, wsum(lsy * exp2_fast((lymax - m_y) * kLog2e)));
+      const float a = wmax(lzmax), c = wmax(lymax);
+      if (ln == 0) {
+        sh.wred[wv][z0 + 0] = a;
+        sh.wred[wv][z0 + 1] = c;
       }
-      put4(sh, 4, __int_as_float(wiz));
-      put4(sh, 5, __int_as_float(wiy));
-      put4(sh, 6, wza);
     }
     __syncthreads();
-    if (tid == 0) {
-      const float tsz = (sh.red[0][2] + sh.red[1][2]) + (sh.red[2][2] + sh.red[3][2]);
-      const float tsy = (sh.red[0][3] + sh.red[1][3]) + (sh.red[2][3] + sh.red[3][3]);
-      int tiz = kBig, tiy = kBig;
-      float tz = 0.f;
-      for (int q = 0; q < 4; ++q) {
-        tiz = min(tiz, __float_as_int(sh.red[q][4]));
-        const int qi = __float_as_int(sh.red[q][5]);
-        if (qi < tiy) {
-          tiy = qi;
-          tz = sh.red[q][6];
+    const float Mzc = fmaxf(fmaxf(sh.wred[0][z0 + 0], sh.wred[1][z0 + 0]), fmaxf(sh.wred[2][z0 + 0], sh.wred[3][z0 + 0]));
+    const float Myc = fmaxf(fmaxf(sh.wred[0][z0 + 1], sh.wred[1][z0 + 1]), fmaxf(sh.wred[2][z0 + 1], sh.wred[3][z0 + 1]));
+
+    // ---- sums relative to 2^fl(chunk max log2 e), lowest indices of the chunk maxima
+    float wsz = 0.f, wsy = 0.f;
+    if constexpr (kSums) {
+      const float cMz = Mzc * kLog2e, cMy = Myc * kLog2e;
+      float lsz = ek[0] * exp2_fast(vm[0].z() * kLog2e - cMz);
+#pragma unroll
+      for (int k = 1; k < K; ++k) lsz = __builtin_fmaf(ek[k], exp2_fast(vm[k].z() * kLog2e - cMz), lsz);
+      wsz = wsum(lsz);
+      wsy = wsum(sy * exp2_fast(ref_y - cMy));
+    }
+    int wiz = kBig, wiy = kBig;
+    float wza = 0.f;
+    {
+      const bool hz = lzmax == Mzc;
+      if (__builtin_amdgcn_ballot_w64(hz)) {  // a wave holding the chunk maximum of z
+        int kk = K;
+#pragma unroll
+        for (int k = K - 1; k >= 0; --k) kk = (vm[k].z() == Mzc) ? k : kk;
+        int iz = kBig;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          if (__builtin_amdgcn_ballot_w64(hz && kk == k)) {
+            if (hz && kk == k) {
+              float x[EPV];
+              In::decode(zr[k], x);
+              iz = (cv0 + lt + k * kThreads) * EPV + first_eq<EPV>(x, Mzc);
+            }
+          }
         }
+        wiz = wmin(iz);
       }
-      sh.out[0] = m_z;
-      sh.out[1] = tsz;
-      sh.out[2] = m_y;
-      sh.out[3] = tsy;
-      sh.out[4] = __int_as_float(tiz);
-      sh.out[5] = __int_as_float(tiy);
-      sh.out[6] = tz;
+      const bool hy = lymax == Myc;
+      if (__builtin_amdgcn_ballot_w64(hy)) {
+        int kk = K;
+#pragma unroll
+        for (int k = K - 1; k >= 0; --k) {
+          float w[EPV];
+          In::decode(ylds[k * kThreads + lt], w);
+          kk = (hy && vmax<EPV>(w) == Myc) ? k : kk;
+        }
+        int iy = kBig;
+        float za = 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          if (__builtin_amdgcn_ballot_w64(hy && kk == k)) {
+            if (hy && kk == k) {
+              float x[EPV], w[EPV];
+              In::decode(zr[k], x);
+              In::decode(ylds[k * kThreads + lt], w);
+              const int e0 = first_eq<EPV>(w, Myc);
+              float zv = x[0];
+#pragma unroll
+              for (int e = 1; e < EPV; ++e) zv = (e == e0) ? x[e] : zv;
+              iy = (cv0 + lt + k * kThreads) * EPV + e0;
+              za = zv;
+            }
+          }
+        }
+        wiy = wmin(iy);
+        wza = wsum(iy == wiy ? za : 0.f);  // the ln holding the index (unique)
+      }
+    }
+    if (ln == 0) {
+      sh.wred[wv][z0 + 2] = wsz;
+      sh.wred[wv][z0 + 3] = wsy;
+      sh.widx[wv][z0 + 0] = wiz;
+      sh.widx[wv][z0 + 1] = wiy;
+      sh.wza[z0 + wv] = wza;
     }
     __syncthreads();
 
-    const uint32_t flag1 = P.flag_base + 2u * (uint32_t)iter;
-    if (P.G > 1) {
-      if (!exchange<kStage1Units>(sh, P, team, chunk, 0, flag1, true)) break;
-    }
-
-    // ---- combine the G chunk partials (each lane takes chunks lane, lane+64, ... in order, then a
-    // fixed DPP tree: identical in every member, deterministic)
-    float Mz, My, Sz, Sy, za;
-    int dtop, atop;
-    if (P.G > 1) {
-      const int lane = tid & 63;
-      float mz = kNegInf, my = kNegInf;
-      for (int c = lane; c < P.G; c += 64) {
-        mz = fmaxf(mz, __uint_as_float(sh.rx[c * kStage1Units + 0]));
-        my = fmaxf(my, __uint_as_float(sh.rx[c * kStage1Units + 2]));
-      }
-      Mz = wmax(mz);
-      My = wmax(my);
-      float lsz = 0.f, lsy = 0.f, lza = 0.f;
-      int liz = kBig, liy = kBig;
-      for (int c = lane; c < P.G; c += 64) {
-        const uint32_t* u = sh.rx + c * kStage1Units;
-        const float mzc = __uint_as_float(u[0]), myc = __uint_as_float(u[2]);
-        if constexpr (MODE != kTop1) {
-          lsz = __builtin_fmaf(__uint_as_float(u[1]), exp2_fast((mzc - Mz) * kLog2e), lsz);
-          lsy = __builtin_fmaf(__uint_as_float(u[3]), exp2_fast((myc - My) * kLog2e), lsy);
+    // ---- exchange 1: wave 0 publishes the chunk values, gathers the members' values and forms the
+    // row constants; the other waves wait at the barrier
+    const uint32_t flag1 = pp->flag_base + 2u * (uint32_t)iter;
+    if (wave == 0) {
+      {
+        const float sz = (sh.wred[0][z0 + 2] + sh.wred[1][z0 + 2]) + (sh.wred[2][z0 + 2] + sh.wred[3][z0 + 2]);
+        const float sy2 = (sh.wred[0][z0 + 3] + sh.wred[1][z0 + 3]) + (sh.wred[2][z0 + 3] + sh.wred[3][z0 + 3]);
+        int ciz = kBig, ciy = kBig;
+        float cza = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          ciz = min(ciz, sh.widx[q][z0 + 0]);
+          if (sh.widx[q][z0 + 1] < ciy) {
+            ciy = sh.widx[q][z0 + 1];
+            cza = sh.wza[z0 + q];
+          }
         }
-        if (liz == kBig && mzc == Mz) liz = (int)u[4];
-        if (liy == kBig && myc == My) {
-          liy = (int)u[5];
-          lza = __uint_as_float(u[6]);
+        if (ln == 0) {
+          sh.part[z0 + 0] = __float_as_uint(Mzc);
+          sh.part[z0 + 1] = __float_as_uint(sz);
+          sh.part[z0 + 2] = __float_as_uint(Myc);
+          sh.part[z0 + 3] = __float_as_uint(sy2);
+          sh.part[z0 + 4] = (uint32_t)ciz;
+          sh.part[z0 + 5] = (uint32_t)ciy;
+          sh.part[z0 + 6] = __float_as_uint(cza);
         }
       }
-      Sz = (MODE != kTop1) ? wsum(lsz) : 0.f;
-      Sy = (MODE != kTop1) ? wsum(lsy) : 0.f;
-      dtop = wmin(liz);
-      atop = wmin(liy);
-      za = wsum(liy == atop ? lza : 0.f);
-    } else {
-      Mz = sh.out[0];
-      Sz = sh.out[1];
-      My = sh.out[2];
-      Sy = sh.out[3];
-      dtop = __float_as_int(sh.out[4]);
-      atop = __float_as_int(sh.out[5]);
-      za = sh.out[6];
+      if (G > 1) {
+        publish<kStage1Units>(units1 + (size_t)chunk * 8, ln, flag1, sh.part + z0);
+        if (!gather_wave<kStage1Units>(sh.rx + z0, units1, G, ln, flag1, pp->spin_limit)) sh.err = 1;
+      }
+      float Mz, My, Sz = 0.f, Sy = 0.f, za;
+      int dtop, atop;
+      if (G > 1) {
+        // ln c combines member c (and c + 64); the members are then reduced in a fixed DPP order
+        float mz = kNegInf, my = kNegInf, lsz = 0.f, lsy = 0.f, lza = 0.f;
+        int liz = kBig, liy = kBig;
+        for (int c = ln; c < G; c += 64) {
+          mz = fmaxf(mz, __uint_as_float(sh.rx[z0 + c * kStage1Units + 0]));
+          my = fmaxf(my, __uint_as_float(sh.rx[z0 + c * kStage1Units + 2]));
+        }
+        Mz = wmax(mz);
+        My = wmax(my);
+        const float cHz = Mz * kLog2e, cHy = My * kLog2e;
+        for (int c = ln; c < G; c += 64) {
+          const uint32_t* u = sh.rx + z0 + c * kStage1Units;
+          const float mzc = __uint_as_float(u[0]), myc = __uint_as_float(u[2]);
+          if constexpr (kSums) {
+            lsz = __builtin_fmaf(__uint_as_float(u[1]), exp2_fast(mzc * kLog2e - cHz), lsz);
+            lsy = __builtin_fmaf(__uint_as_float(u[3]), exp2_fast(myc * kLog2e - cHy), lsy);
+          }
+          if (mzc == Mz) liz = min(liz, (int)u[4]);
+          if (myc == My && (int)u[5] < liy) {
+            liy = (int)u[5];
+            lza = __uint_as_float(u[6]);
+          }
+        }
+        if constexpr (kSums) {
+          Sz = wsum(lsz);
+          Sy = wsum(lsy);
+        }
+        dtop = wmin(liz);
+        atop = wmin(liy);
+        za = wsum(liy == atop ? lza : 0.f);
+      } else {
+        Mz = Mzc;
+        My = Myc;
+        Sz = __uint_as_float(sh.part[z0 + 1]);
+        Sy = __uint_as_float(sh.part[z0 + 3]);
+        dtop = (int)sh.part[z0 + 4];
+        atop = (int)sh.part[z0 + 5];
+        za = __uint_as_float(sh.part[z0 + 6]);
+      }
+      if (ln == 0) {
+        sh.row[z0 + kRowMz] = Mz;
+        sh.row[z0 + kRowMy] = My;
+        sh.row[z0 + kRowDtop] = __int_as_float(dtop);
+        sh.row[z0 + kRowAtop] = __int_as_float(atop);
+        sh.row[z0 + kRowZa] = za;
+        if constexpr (kSums) {
+          // Sz = sum 2^(z log2e - fl(Mz log2e)); ln of sum e^(z - Mz) takes back the rounding of
+          // fl(Mz log2e), which fma recovers exactly
+          const float ln_sz = (log2_fast(Sz) - __builtin_fmaf(Mz, kLog2e, -(Mz * kLog2e))) * kLn2;
+          const float ln_sy = (log2_fast(Sy) - __builtin_fmaf(My, kLog2e, -(My * kLog2e))) * kLn2;
+          sh.row[z0 + kRowLnSz] = ln_sz;
+          sh.row[z0 + kRowLnSy] = ln_sy;
+          sh.row[z0 + kRowDelta] = (Mz - My) + (ln_sz - ln_sy);
+        }
+      }
     }
+    __syncthreads();
+    if (sh.err) break;
 
+    const float Mz = sh.row[z0 + kRowMz];
+    const int dtop = __float_as_int(sh.row[z0 + kRowDtop]);
+    const int atop = __float_as_int(sh.row[z0 + kRowAtop]);
     if constexpr (MODE == kTop1) {
       if (chunk == 0 && tid == 0) {
-        P.target_top1[row] = atop;
-        P.draft_top1[row] = dtop;
+        pp->target_top1[row] = atop;
+        if (pp->draft_top1) pp->draft_top1[row] = dtop;
       }
     } else {
-      const float ln_sz = logf(Sz);
-      const float ln_sy = logf(Sy);
+      const float ln_sz = sh.row[z0 + kRowLnSz];
+      const float delta = sh.row[z0 + kRowDelta];
       RowConst rc;
-      rc.init(Mz, ln_sz, (Mz - My) + (ln_sz - ln_sy));
-      const float delta = rc.delta;
+      rc.init(Mz, ln_sz, delta);
 
-      // ---- phase B. Vector bound: every t_v of a vector is <= p(max z) * max(max(z - y) - delta, 0)
-      // (same monotone p() and subtraction as the element test), so a vector whose bound is <= tau
-      // holds no clipped term and its S / reverse-KL contributions come from E_k, B_k. Vectors near
-      // the peak are summed element by element.
-      const float one_m_delta = 1.f - delta;
-      float s_fast = 0.f, r_fast = 0.f, s_slow = 0.f, r_slow = 0.f;
-      bool slowv[K];
+      // ---- phase B: vectors that pass the bound use their phase-A sums, the rest (near the peak)
+      // are summed element by element
+      float pe = 0.f, pb = 0.f, s_slow = 0.f, r_slow = 0.f;
+      uint32_t slowbits = 0;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const float ub = rc.p(zmv[k]) * fmaxf(dmv[k] - delta, 0.f);
-        slowv[k] = ub > tau;
-        // e-units of vector k (relative to 2^(fl(zmax_k log2e))) -> probabilities
-        const float scale = exp2_fast((zmv[k] * kLog2e - rc.c_hi) - rc.c_lo);
-        s_fast += slowv[k] ? 0.f : scale * __builtin_fmaf(one_m_delta, ek[k], bk[k]);
-        r_fast += slowv[k] ? 0.f : scale * __builtin_fmaf(-delta, ek[k], bk[k]);
-        if (__builtin_amdgcn_ballot_w64(slowv[k])) {
+        const float sc = vector_scale(rc, vm[k].z());
+        const bool slow = vector_may_clip(rc, sc, vm[k].d(), tau_b);
+        slowbits |= (uint32_t)slow << k;
+        const float u = slow ? 0.f : sc;
+        pe = __builtin_fmaf(u, ek[k], pe);
+        pb = __builtin_fmaf(u, bk[k], pb);
+        if (__builtin_amdgcn_ballot_w64(slow)) {
           opaque(zr[k]);
           float x[EPV], w[EPV];
           In::decode(zr[k], x);
-          In::decode(ylds[k * kThreads + tid], w);
-          const int vi = tv + k * kThreads;
+          In::decode(ylds[k * kThreads + lt], w);
+          const int vi = cv0 + lt + k * kThreads;
+          const int nvalid = (lt + k * kThreads < clen) ? min(EPV, pp->vocab - vi * EPV) : 0;
 #pragma unroll
           for (int e = 0; e < EPV; ++e) {
-            const bool valid = slowv[k] && (vi < cv1) && (vi * EPV + e < P.vocab);
+            const bool valid = slow && e < nvalid;
             const float p = rc.p(x[e]);
             const float t = p * ((x[e] - w[e]) - delta);
             const bool clipped = t > tau;
@@ -639,75 +890,89 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
           fence_vals(r_slow, s_slow);
         }
       }
-      put4(sh, 6, wsum(s_fast + s_slow));
-      put4(sh, 7, wsum(r_fast + r_slow));
-      __syncthreads();
-      if (tid == 0) {
-        sh.out[0] = (sh.red[0][6] + sh.red[1][6]) + (sh.red[2][6] + sh.red[3][6]);
-        sh.out[1] = (sh.red[0][7] + sh.red[1][7]) + (sh.red[2][7] + sh.red[3][7]);
+      {
+        const float a = wsum(__builtin_fmaf(1.f - delta, pe, pb) + s_slow);
+        const float c = wsum(__builtin_fmaf(-delta, pe, pb) + r_slow);
+        if (ln == 0) {
+          sh.wred[wv][z0 + 0] = a;
+          sh.wred[wv][z0 + 1] = c;
+        }
       }
       __syncthreads();
-      float S = 0.f, rkl = 0.f;
-      const bool need_rx2 = (MODE == kFused) || chunk == 0;
-      if (P.G > 1) {
-        if (!exchange<kStage2Units>(sh, P, team, chunk, 1, flag1 + 1u, need_rx2)) break;
-        if (need_rx2) {
-          const int lane = tid & 63;
+      // ---- exchange 2 (wave 0) and the row outputs (chunk 0)
+      const bool need_all = (MODE == kFused) || chunk == 0;
+      const uint32_t flag2 = flag1 + 1u;
+      if (wave == 0) {
+        if (ln == 0) {
+          sh.part[z0 + 0] = __float_as_uint((sh.wred[0][z0 + 0] + sh.wred[1][z0 + 0]) + (sh.wred[2][z0 + 0] + sh.wred[3][z0 + 0]));
+          sh.part[z0 + 1] = __float_as_uint((sh.wred[0][z0 + 1] + sh.wred[1][z0 + 1]) + (sh.wred[2][z0 + 1] + sh.wred[3][z0 + 1]));
+        }
+        if (G > 1) {
+          publish<kStage2Units>(units2 + (size_t)chunk * 8, ln, flag2, sh.part + z0);
+          if (need_all && !gather_wave<kStage2Units>(sh.rx + z0, units2, G, ln, flag2, pp->spin_limit)) sh.err = 1;
+        }
+        float S = __uint_as_float(sh.part[z0 + 0]), rkl = __uint_as_float(sh.part[z0 + 1]);
+        if (G > 1 && need_all) {
           float ls = 0.f, lr = 0.f;
-          for (int c = lane; c < P.G; c += 64) {
-            ls += __uint_as_float(sh.rx[c * kStage2Units + 0]);
-            lr += __uint_as_float(sh.rx[c * kStage2Units + 1]);
+          for (int c = ln; c < G; c += 64) {
+            ls += __uint_as_float(sh.rx[z0 + c * kStage2Units + 0]);
+            lr += __uint_as_float(sh.rx[z0 + c * kStage2Units + 1]);
           }
           S = wsum(ls);
           rkl = wsum(lr);
         }
-      } else {
-        S = sh.out[0];
-        rkl = sh.out[1];
+        if (ln == 0) {
+          sh.row[z0 + kRowS] = S;
+          sh.row[z0 + kRowRkl] = rkl;
+          if (chunk == 0) {
+            const float My = sh.row[z0 + kRowMy], ln_sy = sh.row[z0 + kRowLnSy], za = sh.row[z0 + kRowZa];
+            const float ce = (Mz - za) + ln_sz;
+            float* st = pp->row_stats + 8 * (int64_t)row;
+            pp->loss[row] = alpha * rkl + (1.f - alpha) * ce;
+            pp->target_top1[row] = atop;
+            if (pp->draft_top1) pp->draft_top1[row] = dtop;
+            st[0] = Mz + ln_sz;
+            st[1] = My + ln_sy;
+            st[2] = S;
+            st[3] = rkl;
+            st[4] = Mz;
+            st[5] = ln_sz;
+            st[6] = delta;
+            st[7] = ce;
+          }
+        }
       }
-      if (chunk == 0 && tid == 0) {
-        const float ce = (Mz - za) + ln_sz;
-        float* st = P.row_stats + 8 * (int64_t)row;
-        P.loss[row] = alpha * rkl + (1.f - alpha) * ce;
-        P.target_top1[row] = atop;
-        if (P.draft_top1) P.draft_top1[row] = dtop;
-        st[0] = Mz + ln_sz;
-        st[1] = My + ln_sy;
-        st[2] = S;
-        st[3] = rkl;
-        st[4] = Mz;
-        st[5] = ln_sz;
-        st[6] = delta;
-        st[7] = ce;
-      }
+      __syncthreads();
+      if (sh.err) break;
 
       if constexpr (MODE == kFused) {
         // ---- phase C: dz (formulas shared with k_bwd through dz_vector)
         DzConst dc;
-        dc.init(rc, S, alpha, P.grad_loss ? P.grad_loss[row] : 1.f);
-        uint8_t* drow = P.dz + (int64_t)row * P.ld_dz_bytes;
+        dc.init(rc, sh.row[z0 + kRowS], alpha, pp->grad_loss ? pp->grad_loss[row] : 1.f);
+        const __amdgpu_buffer_rsrc_t rd = rsrc(pp->dz + (int64_t)row * pp->ld_dz_bytes + (int64_t)cv0 * VB, clen * VB);
+        __asm__ volatile("" : "+v"(lt));  // fresh offsets: not kept live from the loads
+        // the one vector holding the target top-1 (if it lies in this chunk)
+        const int va = atop / EPV - cv0;
+        const int ka = (va >= 0 && va < clen) ? va / kThreads : -1;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
           opaque(zr[k]);
           float x[EPV], w[EPV], o[EPV];
           In::decode(zr[k], x);
-          In::decode(ylds[k * kThreads + tid], w);
-          dz_vector<EPV>(x, w, slowv[k], __builtin_amdgcn_ballot_w64(slowv[k]) != 0, rc, dc, tau, o);
-          const int vi = tv + k * kThreads;
-          const int g0 = vi * EPV;
-          fix_target<EPV>(o, g0, atop, dc.wce);
+          In::decode(ylds[k * kThreads + lt], w);
+          const bool slow = (slowbits >> k) & 1u;
+          dz_vector<EPV>(x, w, slow, __builtin_amdgcn_ballot_w64(slow) != 0, rc, dc, tau, o);
+          const int vi = cv0 + lt + k * kThreads;
+          if (k == ka) fix_target<EPV>(o, vi * EPV, atop, dc.wce);
 #pragma unroll
           for (int e = 0; e < EPV; e += 4) fence_vals(o[e], o[e + 1], o[e + 2], o[e + 3]);
-          uint8_t* dst = drow + (int64_t)g0 * OSZ;
-          if ((k + 1) * kThreads <= clen && !tail_chunk) {  // uniform: every lane holds a full vector
-            store_vec<OutBF16, EPV>(dst, o);
-          } else if (vi < cv1) {
-            if (g0 + EPV <= P.vocab) {
-              store_vec<OutBF16, EPV>(dst, o);
-            } else {
-              store_partial<OutBF16, EPV>(dst, o, P.vocab - g0);
-            }
+          int off = (lt + k * kThreads) * VB;  // past num_records for lanes beyond the chunk: dropped
+          if (tail_chunk && vi == pp->nvec - 1) {  // partial last vector: element stores
+            store_partial<OutBF16, EPV>(pp->dz + (int64_t)row * pp->ld_dz_bytes + (int64_t)vi * VB, o,
+                                        pp->vocab - vi * EPV);
+            off = 0x7fffffff & ~(VB - 1);
           }
+          buf_store_vec<OutBF16, EPV>(rd, off, o);
         }
       }
     }
@@ -723,7 +988,7 @@ template <class In, bool OutBF16>
 __global__ void __launch_bounds__(kThreads) k_bwd(BwdParams P) {
   constexpr int EPV = In::EPV;
   constexpr int OSZ = OutBF16 ? 2 : 4;
-  const int row = blockIdx.y;
+  const int row = block_id_y();
   const float* st = P.row_stats + 8 * (int64_t)row;
   RowConst rc;
   rc.init(st[4], st[5], st[6]);
@@ -734,7 +999,7 @@ __global__ void __launch_bounds__(kThreads) k_bwd(BwdParams P) {
   const uint4* zrow = (const uint4*)(P.z + (int64_t)row * P.ld_bytes);
   const uint4* yrow = (const uint4*)(P.y + (int64_t)row * P.ld_bytes);
   uint8_t* drow = P.dz + (int64_t)row * P.ld_dz_bytes;
-  const int v0 = blockIdx.x * (kThreads * kBwdVecPerThread) + threadIdx.x;
+  const int v0 = block_id_x() * (kThreads * kBwdVecPerThread) + thread_id();
   uint4 zr[kBwdVecPerThread], yr[kBwdVecPerThread];
 #pragma unroll
   for (int k = 0; k < kBwdVecPerThread; ++k) {
@@ -764,13 +1029,11 @@ __global__ void __launch_bounds__(kThreads) k_bwd(BwdParams P) {
     In::decode(zr[k], x);
     In::decode(yr[k], w);
     // the fused kernel's vector bound, recomputed: same decisions, bit-identical dz
-    float zm = x[0], dm = x[0] - w[0];
+    float d[EPV];
 #pragma unroll
-    for (int e = 1; e < EPV; ++e) {
-      zm = fmaxf(zm, x[e]);
-      dm = fmaxf(dm, x[e] - w[e]);
-    }
-    const bool slow = rc.p(zm) * fmaxf(dm - rc.delta, 0.f) > tau;
+    for (int e = 0; e < EPV; ++e) d[e] = x[e] - w[e];
+    const float sc = vector_scale(rc, vmax<EPV>(x));
+    const bool slow = vector_may_clip(rc, sc, kept_dmax<EPV>(vmax<EPV>(d)), tau * kBoundShrink);
     dz_vector<EPV>(x, w, slow, __builtin_amdgcn_ballot_w64(slow) != 0, rc, dc, tau, o);
     const int g0 = vi * EPV;
     fix_target<EPV>(o, g0, atop, dc.wce);
@@ -788,7 +1051,7 @@ __global__ void __launch_bounds__(kThreads) k_bwd(BwdParams P) {
 // ---------------------------------------------------------------- accept length per packed block
 
 __global__ void __launch_bounds__(kThreads) k_accept(AcceptParams P) {
-  const int b = blockIdx.x * kThreads + threadIdx.x;
+  const int b = block_id_x() * kThreads + thread_id();
   if (b >= P.n_blocks) return;
   const int start = P.offsets[b], end = P.offsets[b + 1];
   uint32_t fl = 0;
@@ -808,10 +1071,8 @@ __global__ void __launch_bounds__(kThreads) k_accept(AcceptParams P) {
   if (fl) atomicOr(P.flags, fl);
 }
 
-__global__ void k_fill_u32(uint32_t* dst, uint32_t value, size_t count) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x) {
-    dst[i] = value;
-  }
+__global__ void __launch_bounds__(kThreads) k_fill_u32(uint32_t* dst, uint32_t value, size_t count, size_t stride) {
+  for (size_t i = block_id_x() * (size_t)kThreads + thread_id(); i < count; i += stride) dst[i] = value;
 }
 
 // ---------------------------------------------------------------- instantiation tables
@@ -871,7 +1132,8 @@ hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, size_t count, hipStrea
   size_t blocks = (count + kThreads - 1) / kThreads;
   if (blocks > 1024) blocks = 1024;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(kThreads), 0, s, dst, value, count);
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(kThreads), 0, s, dst, value, count,
+                     blocks * (size_t)kThreads);
   return hipGetLastError();
 }
 
