@@ -12,7 +12,8 @@ HBM. Prints one JSON line:
 * roofline: the row-team kernel (the only kernel that touches the logits) timed with HIP events on
   its stream over K launches without verification; achieved = algorithmic bytes per launch
   (read z and y once, write dz once, plus 44 bytes of per-row outputs) / average launch time,
-  against the MI355X HBM peak of 8 TB/s. traffic = HBM bytes per launch from the rocprofv3
+  against the MI355X HBM peak of 8 TB/s. measured_stream_gbs: the library's stream probe (the same
+  two-reads-one-write pattern over the same buffers, no arithmetic), timed the same way. traffic = HBM bytes per launch from the rocprofv3
   FETCH_SIZE / WRITE_SIZE counters recorded in profiles/ for the current kernel source (null if the
   kernel changed since they were taken).
 * cpu_baseline: the float64 oracle (loss, gradient, top-1s, accept lengths) on a bounded sample of
@@ -215,6 +216,25 @@ def main():
         print("[bench] device flags raised during the timed region", file=sys.stderr)
         sys.exit(1)
 
+    # achievable bandwidth of the same traffic pattern (read z and y, write a dz-sized buffer) with
+    # no arithmetic: the stream probe of the library, timed the same way
+    stream_gbs = None
+    if not args.profile:
+        zb = z.contiguous().view(torch.uint8).view(-1)
+        yb = y.contiguous().view(torch.uint8).view(-1)
+        dzb = out["dz"].view(torch.uint8).view(-1)
+        if dzb.numel() != zb.numel():
+            dzb = torch.empty_like(zb)
+        opd.stream_probe(zb, yb, dzb)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            opd.stream_probe(zb, yb, dzb)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        probe_ms = ev0.elapsed_time(ev1) / args.steps
+        stream_gbs = 3 * zb.numel() / (probe_ms * 1e-3) / 1e9
+        del zb, yb, dzb
+
     if args.profile:
         # calibration copy: 1 GiB read + 1 GiB written by a plain copy kernel
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -263,6 +283,10 @@ def main():
             "kernel": "k_team (fused mode)",
             "kernel_ms": kernel_ms,
             "algorithmic_bytes_per_launch": alg_bytes,
+            # the same read/read/write stream with no arithmetic (opd_stream_probe): the achievable
+            # bandwidth for this traffic pattern on this device, and the kernel's share of it
+            "measured_stream_gbs": stream_gbs,
+            "frac_of_measured_stream": (achieved / stream_gbs) if stream_gbs else None,
         },
         "cpu_baseline": cpu,
     }

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     opd_loss_fwd,
     read_flags,
     set_spin_limit,
+    stream_probe,
     verify_accept_len,
     workspace,
 )

@@ -27,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "verify_accept_len",
     "opd_fused_fwd_bwd_verify",
     "opd_read_flags",
+    "opd_stream_probe",
     "opd_set_spin_limit",
     "opd_status_string",
     "opd_last_error",
@@ -75,6 +76,8 @@ def load_library(require_torch_runtime: bool = True) -> ctypes.CDLL:
                                                  vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, sz, vp]
         lib.opd_read_flags.restype = i32
         lib.opd_read_flags.argtypes = [vp, sz, i32, ctypes.POINTER(ctypes.c_uint32), vp]
+        lib.opd_stream_probe.restype = i32
+        lib.opd_stream_probe.argtypes = [vp, vp, vp, sz, vp]
         lib.opd_set_spin_limit.restype = None
         lib.opd_set_spin_limit.argtypes = [ctypes.c_uint32]
         lib.opd_status_string.restype = ctypes.c_char_p
@@ -172,6 +175,18 @@ def read_flags(ws=None, clear: bool = False, device=None) -> int:
     out = ctypes.c_uint32(0)
     _check("opd_read_flags", lib.opd_read_flags(ws.data_ptr(), ws.numel(), int(clear), ctypes.byref(out), _stream(ws.device)))
     return int(out.value)
+
+
+def stream_probe(a, b, c) -> None:
+    """c = a XOR b over the bytes of three equally sized, 16-byte aligned device tensors (bandwidth probe)."""
+    lib = load_library()
+    nbytes = a.numel() * a.element_size()
+    if b.numel() * b.element_size() != nbytes or c.numel() * c.element_size() != nbytes:
+        raise ValueError("a, b and c must hold the same number of bytes")
+    if not (a.is_contiguous() and b.is_contiguous() and c.is_contiguous()):
+        raise ValueError("a, b and c must be contiguous")
+    _check("opd_stream_probe", lib.opd_stream_probe(a.data_ptr(), b.data_ptr(), c.data_ptr(), ctypes.c_size_t(nbytes),
+                                                    _stream(a.device)))
 
 
 def _blocks(offsets, lengths):

@@ -351,6 +351,17 @@ opd_status_t opd_read_flags(void* ws, size_t ws_bytes, int clear, uint32_t* flag
   return OPD_OK;
 }
 
+opd_status_t opd_stream_probe(const void* a, const void* b, void* c, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return OPD_OK;
+  if (!a || !b || !c) return fail(OPD_ERR_NULL, "a, b and c must be non-NULL");
+  if (bytes % 16) return fail(OPD_ERR_SHAPE, "bytes must be a multiple of 16");
+  if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) | reinterpret_cast<uintptr_t>(c)) % 16)
+    return fail(OPD_ERR_ALIGN, "buffers must be 16-byte aligned");
+  hipError_t e = opd::launch_stream_probe(a, b, c, bytes / 16, stream);
+  if (e != hipSuccess) return hip_fail(e, "stream probe launch");
+  return OPD_OK;
+}
+
 void opd_set_spin_limit(uint32_t spins) { g_spin_limit.store(spins); }
 
 const char* opd_status_string(opd_status_t s) {

@@ -88,5 +88,6 @@ hipError_t team_occupancy(int mode, int in_bf16, int out_bf16, int K, int* block
 hipError_t launch_bwd(const BwdParams& p, int in_bf16, int out_bf16, hipStream_t s);
 hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, size_t count, hipStream_t s);
+hipError_t launch_stream_probe(const void* a, const void* b, void* c, size_t n_vec, hipStream_t s);
 
 }  // namespace opd

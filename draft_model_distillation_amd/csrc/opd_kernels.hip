@@ -1075,6 +1075,16 @@ __global__ void __launch_bounds__(kThreads) k_fill_u32(uint32_t* dst, uint32_t v
   for (size_t i = block_id_x() * (size_t)kThreads + thread_id(); i < count; i += stride) dst[i] = value;
 }
 
+// Two nontemporal 16-byte reads and one write per vector, grid-stride: the fused path's HBM pattern
+// with no arithmetic, for the achievable-bandwidth figure reported beside the kernels.
+__global__ void __launch_bounds__(kThreads) k_stream_probe(const uint4* a, const uint4* b, uint8_t* c, size_t n,
+                                                           size_t stride) {
+  for (size_t i = block_id_x() * (size_t)kThreads + thread_id(); i < n; i += stride) {
+    const uint4 x = load_nt(a + i), y = load_nt(b + i);
+    store_nt(c + 16 * i, x.x ^ y.x, x.y ^ y.y, x.z ^ y.z, x.w ^ y.w);
+  }
+}
+
 // ---------------------------------------------------------------- instantiation tables
 
 template <int MODE>
@@ -1126,6 +1136,16 @@ hipError_t launch_accept(const AcceptParams& p, hipStream_t s) {
   AcceptParams copy = p;
   void* args[] = {&copy};
   return hipLaunchKernel((void*)k_accept, grid, dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_stream_probe(const void* a, const void* b, void* c, size_t n_vec, hipStream_t s) {
+  if (n_vec == 0) return hipSuccess;
+  // 512 workgroups (2 per CU) streamed fastest for this pattern on MI355X
+  size_t blocks = (n_vec + kThreads - 1) / kThreads;
+  if (blocks > 512) blocks = 512;
+  hipLaunchKernelGGL(k_stream_probe, dim3((unsigned)blocks), dim3(kThreads), 0, s, (const uint4*)a, (const uint4*)b,
+                     (uint8_t*)c, n_vec, blocks * (size_t)kThreads);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, size_t count, hipStream_t s) {

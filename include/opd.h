@@ -146,6 +146,14 @@ opd_status_t opd_fused_fwd_bwd_verify(const void* z, const void* y, opd_dtype_t 
  * `clear` is non-zero. Errors: OPD_ERR_NULL, OPD_ERR_WORKSPACE, OPD_ERR_HIP. */
 opd_status_t opd_read_flags(void* ws, size_t ws_bytes, int clear, uint32_t* flags, hipStream_t stream);
 
+/* Measurement aid, not part of the method: streams the HBM traffic pattern of the fused path --
+ * two 16-byte reads and one 16-byte write per vector, nontemporal -- with no arithmetic beyond
+ * c = a XOR b, so that its rate is the achievable bandwidth for that pattern on this device.
+ *   a, b   device buffers of `bytes` bytes (read); c device buffer of `bytes` bytes (written).
+ *   bytes  multiple of 16; the three pointers 16-byte aligned; 0 is a no-op.
+ * Errors: OPD_ERR_NULL, OPD_ERR_SHAPE (bytes not a multiple of 16), OPD_ERR_ALIGN, OPD_ERR_HIP. */
+opd_status_t opd_stream_probe(const void* a, const void* b, void* c, size_t bytes, hipStream_t stream);
+
 /* Debug knob for tests of the failure path: caps every cross-workgroup wait at `spins` polls
  * (0 restores the default bound). Affects launches made after the call, process-wide. */
 void opd_set_spin_limit(uint32_t spins);

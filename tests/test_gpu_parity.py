@@ -415,3 +415,20 @@ def test_spin_timeout_is_reported_not_hung(lib):
     assert lib.read_flags(clear=True) == 0
     if flags == 0:
         assert torch.equal(out["loss"], out2["loss"])
+
+
+def test_stream_probe_xor(lib):
+    """The bandwidth probe writes a XOR b over the whole buffer, including a ragged tail."""
+    import torch
+
+    g = torch.Generator().manual_seed(5)
+    n = (1 << 20) + 48  # bytes: whole 16-byte vectors, not a multiple of the grid stride
+    a = torch.randint(0, 256, (n,), dtype=torch.uint8, generator=g)
+    b = torch.randint(0, 256, (n,), dtype=torch.uint8, generator=g)
+    ad, bd = a.cuda(), b.cuda()
+    cd = torch.full((n + 16,), 7, dtype=torch.uint8, device="cuda")
+    _say("stream probe")
+    lib.stream_probe(ad, bd, cd[:n])
+    torch.cuda.synchronize()
+    assert torch.equal(cd[:n].cpu(), a ^ b)
+    assert torch.all(cd[n:] == 7)
