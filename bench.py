@@ -235,6 +235,18 @@ def main():
         stream_gbs = 3 * zb.numel() / (probe_ms * 1e-3) / 1e9
         del zb, yb, dzb
 
+    # length-head epilogue (a separate small kernel) on this step's top-1s, one logit per block
+    head_us = None
+    if not args.profile and len(lens) > 0:
+        h = torch.linspace(-3.0, 3.0, len(lens), device=dev)
+        opd.length_head_loss(out["target_top1"], out["draft_top1"], off, h, ws=ws)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            opd.length_head_loss(out["target_top1"], out["draft_top1"], off, h, ws=ws)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        head_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+
     if args.profile:
         # calibration copy: 1 GiB read + 1 GiB written by a plain copy kernel
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -289,6 +301,9 @@ def main():
             "frac_of_measured_stream": (achieved / stream_gbs) if stream_gbs else None,
         },
         "cpu_baseline": cpu,
+        # next-row kernels timed beside the step (not part of it): the length-head epilogue per
+        # launch over this workload's blocks (includes the binding's output allocation)
+        "extras": {"length_head_epilogue_us": head_us},
     }
     print(json.dumps(result), flush=True)
 

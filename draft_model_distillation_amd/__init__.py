@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     OPD_FLAG_NEG_L,
     OPD_FLAG_SPIN_TIMEOUT,
     OpdError,
+    length_head_loss,
     library_path,
     load_library,
     opd_fused_fwd_bwd_verify,

@@ -27,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "verify_accept_len",
     "opd_fused_fwd_bwd_verify",
     "opd_read_flags",
+    "opd_length_head_loss",
     "opd_stream_probe",
     "opd_set_spin_limit",
     "opd_status_string",
@@ -76,6 +77,8 @@ def load_library(require_torch_runtime: bool = True) -> ctypes.CDLL:
                                                  vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, sz, vp]
         lib.opd_read_flags.restype = i32
         lib.opd_read_flags.argtypes = [vp, sz, i32, ctypes.POINTER(ctypes.c_uint32), vp]
+        lib.opd_length_head_loss.restype = i32
+        lib.opd_length_head_loss.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.opd_stream_probe.restype = i32
         lib.opd_stream_probe.argtypes = [vp, vp, vp, sz, vp]
         lib.opd_set_spin_limit.restype = None
@@ -175,6 +178,29 @@ def read_flags(ws=None, clear: bool = False, device=None) -> int:
     out = ctypes.c_uint32(0)
     _check("opd_read_flags", lib.opd_read_flags(ws.data_ptr(), ws.numel(), int(clear), ctypes.byref(out), _stream(ws.device)))
     return int(out.value)
+
+
+def length_head_loss(target_top1, draft_top1, offsets, head_logit, grad=None, ws=None) -> dict:
+    """Length-head epilogue per packed block: accept_full i32, label f32, loss f32, dlogit f32."""
+    torch = _torch()
+    lib = load_library()
+    dev = head_logit.device
+    n_blocks = int(offsets.numel()) - 1
+    if int(head_logit.numel()) != n_blocks or (grad is not None and int(grad.numel()) != n_blocks):
+        raise ValueError("head_logit (and grad) must have one entry per block")
+    ws = workspace(dev) if ws is None else ws
+    out = {
+        "accept_full": torch.empty(n_blocks, dtype=torch.int32, device=dev),
+        "label": torch.empty(n_blocks, dtype=torch.float32, device=dev),
+        "loss": torch.empty(n_blocks, dtype=torch.float32, device=dev),
+        "dlogit": torch.empty(n_blocks, dtype=torch.float32, device=dev),
+    }
+    _check("opd_length_head_loss", lib.opd_length_head_loss(
+        target_top1.data_ptr(), draft_top1.data_ptr(), int(target_top1.numel()), offsets.data_ptr(), n_blocks,
+        head_logit.data_ptr(), None if grad is None else grad.data_ptr(), out["accept_full"].data_ptr(),
+        out["label"].data_ptr(), out["loss"].data_ptr(), out["dlogit"].data_ptr(), ws.data_ptr(), ws.numel(),
+        _stream(dev)))
+    return out
 
 
 def stream_probe(a, b, c) -> None:

@@ -18,11 +18,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libopd_mi355x.so"
-SOURCES = ["opd_kernels.hip", "opd_api.cpp"]
-# Kernels only: the VALU runs with the IEEE mode bit clear, so max/min need no NaN-quieting
+SOURCES = ["opd_kernels.hip", "opd_epilogue.hip", "opd_api.cpp"]
+# Row kernels only: the VALU runs with the IEEE mode bit clear, so max/min need no NaN-quieting
 # canonicalisation of their operands (inputs are finite by contract). The host file keeps IEEE NaN
-# semantics for its argument checks.
+# semantics for its argument checks, and the epilogue file the device library's accurate exp/log.
 KERNEL_ONLY = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
+IEEE_OFF_SOURCES = {"opd_kernels.hip"}
 
 COMMON = [
     "--offload-arch=gfx950",
@@ -56,7 +57,9 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        lang = ["-x", "hip", *KERNEL_ONLY] if src.endswith(".hip") else []
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        if src in IEEE_OFF_SOURCES:
+            lang += KERNEL_ONLY
         cmd = [cc, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -332,6 +332,36 @@ opd_status_t opd_fused_fwd_bwd_verify(const void* z, const void* y, opd_dtype_t 
   return run_accept(blocks, n_rows, draft_top1, target_top1, accept_len, ws, stream);
 }
 
+opd_status_t opd_length_head_loss(const int32_t* target_top1, const int32_t* draft_top1, int64_t n_rows,
+                                  const int32_t* offsets, int32_t n_blocks, const float* head_logit,
+                                  const float* grad, int32_t* accept_full, float* label, float* loss,
+                                  float* dlogit, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (n_rows < 0 || n_rows > INT32_MAX) return fail(OPD_ERR_SHAPE, "n_rows out of range");
+  if (n_blocks < 0) return fail(OPD_ERR_SHAPE, "n_blocks must be >= 0");
+  if (n_blocks == 0) return OPD_OK;
+  if (!offsets || !head_logit || !accept_full || !label || !loss || !dlogit)
+    return fail(OPD_ERR_NULL, "offsets, head_logit and the four outputs must be non-NULL");
+  if (n_rows > 0 && (!target_top1 || !draft_top1)) return fail(OPD_ERR_NULL, "top-1 inputs must be non-NULL");
+  opd_status_t s = check_ws(ws, ws_bytes);
+  if (s != OPD_OK) return s;
+  opd::LengthHeadParams p;
+  p.draft_top1 = draft_top1;
+  p.target_top1 = target_top1;
+  p.offsets = offsets;
+  p.n_blocks = n_blocks;
+  p.n_rows = (int32_t)n_rows;
+  p.head_logit = head_logit;
+  p.grad = grad;
+  p.accept_full = accept_full;
+  p.label = label;
+  p.loss = loss;
+  p.dlogit = dlogit;
+  p.flags = static_cast<uint32_t*>(ws);
+  hipError_t e = opd::launch_length_head(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "length-head kernel launch");
+  return OPD_OK;
+}
+
 opd_status_t opd_read_flags(void* ws, size_t ws_bytes, int clear, uint32_t* flags, hipStream_t stream) {
   if (!flags) return fail(OPD_ERR_NULL, "flags must be non-NULL");
   opd_status_t s = check_ws(ws, ws_bytes);

@@ -81,6 +81,21 @@ struct AcceptParams {
   uint32_t* flags;
 };
 
+struct LengthHeadParams {
+  const int32_t* draft_top1;
+  const int32_t* target_top1;
+  const int32_t* offsets;
+  int32_t n_blocks;
+  int32_t n_rows;
+  const float* head_logit;
+  const float* grad;  // nullable
+  int32_t* accept_full;
+  float* label;
+  float* loss;
+  float* dlogit;
+  uint32_t* flags;
+};
+
 // in_bf16: 1 if z/y are bf16 (else fp32); out_bf16: 1 if dz is bf16 (else fp32); K: slots/thread.
 hipError_t launch_team(const TeamParams& p, int mode, int in_bf16, int out_bf16, int K, int grid,
                        hipStream_t s);
@@ -89,5 +104,6 @@ hipError_t launch_bwd(const BwdParams& p, int in_bf16, int out_bf16, hipStream_t
 hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, size_t count, hipStream_t s);
 hipError_t launch_stream_probe(const void* a, const void* b, void* c, size_t n_vec, hipStream_t s);
+hipError_t launch_length_head(const LengthHeadParams& p, hipStream_t s);  // opd_epilogue.hip
 
 }  // namespace opd

@@ -142,6 +142,27 @@ opd_status_t opd_fused_fwd_bwd_verify(const void* z, const void* y, opd_dtype_t 
                                       int32_t* accept_len, void* ws, size_t ws_bytes,
                                       hipStream_t stream);
 
+/*
+ * Length-head epilogue of verification ("AdaFlash: Adaptive Speculative Decoding with Online
+ * Self-Improvement for High-Concurrency LLM Inference", section "2. Adaptive Length Head for
+ * Token-Level Variance": the head predicts a draft block's acceptance rate, and the true rate after
+ * verification is its free supervision signal). From the top-1s of a packed batch (as produced by
+ * opd_fused_fwd_bwd_verify or verify_accept_len), per block b = rows offsets[b] .. offsets[b+1]-1:
+ *   accept_full[b] int32 out: longest prefix of the block's n_b rows with draft_top1 == target_top1
+ *                  (all rows: not capped by the verification budget L);
+ *   label[b]       f32 out: accept_full[b] / n_b, 0 for an empty block;
+ *   loss[b]        f32 out: binary cross entropy of sigmoid(head_logit[b]) against label[b];
+ *   dlogit[b]      f32 out: grad[b] * (sigmoid(head_logit[b]) - label[b]); grad may be NULL (= 1).
+ *   target_top1, draft_top1 [n_rows] int32 device inputs; offsets int32[n_blocks + 1] device;
+ *   head_logit [n_blocks] f32 device input. All device pointers, owned by the caller.
+ * A block with decreasing or out-of-range offsets gets 0 outputs and raises OPD_FLAG_BAD_OFFSETS.
+ * Errors: OPD_ERR_NULL, OPD_ERR_SHAPE (n_rows / n_blocks), OPD_ERR_WORKSPACE, OPD_ERR_HIP.
+ */
+opd_status_t opd_length_head_loss(const int32_t* target_top1, const int32_t* draft_top1, int64_t n_rows,
+                                  const int32_t* offsets, int32_t n_blocks, const float* head_logit,
+                                  const float* grad, int32_t* accept_full, float* label, float* loss,
+                                  float* dlogit, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Reads the sticky device flag word of a workspace (synchronises `stream`); clears it when
  * `clear` is non-zero. Errors: OPD_ERR_NULL, OPD_ERR_WORKSPACE, OPD_ERR_HIP. */
 opd_status_t opd_read_flags(void* ws, size_t ws_bytes, int clear, uint32_t* flags, hipStream_t stream);

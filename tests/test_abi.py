@@ -115,3 +115,14 @@ def test_stream_probe_validation(lib):
     assert lib.opd_stream_probe(P, P, P, 40, None) == 2
     assert lib.opd_stream_probe(P, P + 8, P, 64, None) == 4
     assert lib.opd_stream_probe(None, None, None, 0, None) == 0
+
+
+def test_length_head_validation(lib):
+    ws = lib.opd_workspace_size()
+    # no blocks: nothing to do, NULL everything is fine
+    assert lib.opd_length_head_loss(None, None, 0, None, 0, None, None, None, None, None, None, WS, ws, None) == 0
+    assert lib.opd_length_head_loss(P, P, 4, P, -1, P, None, P, P, P, P, WS, ws, None) == 2
+    assert lib.opd_length_head_loss(P, P, -1, P, 2, P, None, P, P, P, P, WS, ws, None) == 2
+    assert lib.opd_length_head_loss(P, P, 4, P, 2, P, None, P, P, None, P, WS, ws, None) == 1
+    assert lib.opd_length_head_loss(None, P, 4, P, 2, P, None, P, P, P, P, WS, ws, None) == 1
+    assert lib.opd_length_head_loss(P, P, 4, P, 2, P, None, P, P, P, P, WS, 100, None) == 6

@@ -432,3 +432,93 @@ def test_stream_probe_xor(lib):
     torch.cuda.synchronize()
     assert torch.equal(cd[:n].cpu(), a ^ b)
     assert torch.all(cd[n:] == 7)
+
+
+# ------------------------------------------------------------------ length-head epilogue
+
+# Tolerances of the fp32 epilogue against the float64 oracle: the label is one correctly rounded
+# division (1 ulp); the loss is two non-negative softplus terms from expf / log1pf (a few ulps each,
+# no cancellation); the gradient sigmoid(h) - label cancels near the optimum, so it is held to an
+# absolute bound of a few ulps of 1, scaled by the weight.
+LH_LABEL_REL = 2.0 ** -23
+LH_LOSS_REL = 2e-6
+LH_DLOGIT_ABS = 3e-7
+
+
+def _check_length_head(got, ref, grad=None):
+    import torch  # noqa: F401
+
+    acc = got["accept_full"].cpu().numpy()
+    lab = got["label"].cpu().numpy().astype(np.float64)
+    loss = got["loss"].cpu().numpy().astype(np.float64)
+    dl = got["dlogit"].cpu().numpy().astype(np.float64)
+    assert np.array_equal(acc, ref["accept_full"])
+    assert np.all(np.abs(lab - ref["label"]) <= LH_LABEL_REL * np.abs(ref["label"]))
+    assert np.all(np.abs(loss - ref["loss"]) <= LH_LOSS_REL * np.abs(ref["loss"]) + 1e-37)
+    w = np.ones_like(dl) if grad is None else np.maximum(1.0, np.abs(grad))
+    assert np.all(np.abs(dl - ref["dlogit"]) <= LH_DLOGIT_ABS * w)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_length_head_random_blocks(lib, seed):
+    import torch
+
+    from oracle import length_head as LH
+
+    rng = np.random.default_rng(100 + seed)
+    nb = rng.integers(0, 17, size=300)
+    nb[:5] = [0, 1, 16, 0, 16]
+    off = np.concatenate([[0], np.cumsum(nb)]).astype(np.int32)
+    n = int(off[-1])
+    a = rng.integers(0, 50, n).astype(np.int32)
+    d = np.where(rng.random(n) < 0.85, a, rng.integers(0, 50, n)).astype(np.int32)
+    h = rng.normal(0, 4, nb.size).astype(np.float32)
+    h[:8] = [0.0, 60.0, -60.0, 20.0, -20.0, 1e-6, -1e-6, 3.0]
+    grad = None if seed == 0 else rng.normal(0, 2, nb.size).astype(np.float32)
+    _say(f"length head seed={seed} blocks={nb.size} rows={n}")
+    out = lib.length_head_loss(torch.from_numpy(a).cuda(), torch.from_numpy(d).cuda(), torch.from_numpy(off).cuda(),
+                               torch.from_numpy(h).cuda(), None if grad is None else torch.from_numpy(grad).cuda())
+    torch.cuda.synchronize()
+    assert lib.read_flags(clear=True) == 0
+    ref = LH.length_head_epilogue(d, a, off, h.astype(np.float64), None if grad is None else grad.astype(np.float64))
+    _check_length_head(out, ref, grad)
+
+
+def test_length_head_malformed_offsets_flag(lib):
+    import torch
+
+    from oracle import length_head as LH
+
+    a = np.array([1, 2, 3, 4, 5], dtype=np.int32)
+    d = np.array([1, 2, 0, 4, 5], dtype=np.int32)
+    off = np.array([0, 3, 2, 5, 9], dtype=np.int32)  # block 1 decreasing, block 3 past the rows
+    h = np.array([0.5, -1.0, 2.0, 0.0], dtype=np.float32)
+    _say("length head malformed offsets")
+    out = lib.length_head_loss(torch.from_numpy(a).cuda(), torch.from_numpy(d).cuda(), torch.from_numpy(off).cuda(),
+                               torch.from_numpy(h).cuda())
+    torch.cuda.synchronize()
+    assert lib.read_flags(clear=True) == lib.OPD_FLAG_BAD_OFFSETS
+    ref = LH.length_head_epilogue(d, a, off, h.astype(np.float64))
+    assert ref["flags"] == LH.LEN_FLAG_BAD_OFFSETS
+    _check_length_head(out, ref)
+
+
+def test_length_head_on_fused_packed_batch(lib):
+    """The epilogue on the top-1s the fused call produced for the packed ragged batch."""
+    import torch
+
+    from oracle import length_head as LH
+
+    wl = synth.make("packed")
+    _say(f"length head on packed fused outputs rows={wl.n_rows}")
+    z, y, off, lens, out = _run_fused(lib, wl, wl.recipe.dz_dtype)
+    rng = np.random.default_rng(7)
+    h = torch.from_numpy(rng.normal(0, 2, len(wl.lengths)).astype(np.float32)).cuda()
+    res = lib.length_head_loss(out["target_top1"], out["draft_top1"], off, h)
+    torch.cuda.synchronize()
+    assert lib.read_flags(clear=True) == 0
+    ref = LH.length_head_epilogue(out["draft_top1"].cpu().numpy(), out["target_top1"].cpu().numpy(), wl.offsets,
+                                  h.cpu().numpy().astype(np.float64))
+    _check_length_head(res, ref)
+    # the uncapped prefix bounds the L-capped accept length from above
+    assert np.all(res["accept_full"].cpu().numpy() >= out["accept_len"].cpu().numpy())
