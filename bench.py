@@ -247,6 +247,14 @@ def main():
         torch.cuda.synchronize()
         head_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
 
+    # host packer: first fit of the workload's requests (their lengths, in order) under a budget
+    # of half the workload's rows, per call through the binding
+    lengths_np = np.diff(off.cpu().numpy())
+    t_pack = time.perf_counter()
+    for _ in range(200):
+        opd.pack_first_fit(lengths_np, int(lengths_np.sum()) // 2)
+    pack_us = (time.perf_counter() - t_pack) * 1e6 / 200
+
     if args.profile:
         # calibration copy: 1 GiB read + 1 GiB written by a plain copy kernel
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -301,9 +309,11 @@ def main():
             "frac_of_measured_stream": (achieved / stream_gbs) if stream_gbs else None,
         },
         "cpu_baseline": cpu,
-        # next-row kernels timed beside the step (not part of it): the length-head epilogue per
-        # launch over this workload's blocks (includes the binding's output allocation)
-        "extras": {"length_head_epilogue_us": head_us},
+        # next-row pieces timed beside the step (not part of it): the length-head epilogue per launch
+        # over this workload's blocks (includes the binding's output allocation) and the host
+        # packer per call over this workload's requests
+        "extras": {"length_head_epilogue_us": head_us, "host_packer_us": pack_us,
+                   "packer_requests": int(lengths_np.size)},
     }
     print(json.dumps(result), flush=True)
 

@@ -10,6 +10,7 @@ take torch device tensors and enqueue on torch's current stream.
 
 from ._binding import (  # noqa: F401
     EXPORTED_SYMBOLS,
+    CapacityEstimate,
     OPD_BF16,
     OPD_F32,
     OPD_FLAG_BAD_OFFSETS,
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     opd_fused_fwd_bwd_verify,
     opd_loss_bwd,
     opd_loss_fwd,
+    pack_first_fit,
     read_flags,
     set_spin_limit,
     stream_probe,

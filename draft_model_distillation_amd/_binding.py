@@ -28,6 +28,9 @@ EXPORTED_SYMBOLS = (
     "opd_fused_fwd_bwd_verify",
     "opd_read_flags",
     "opd_length_head_loss",
+    "opd_capacity_init",
+    "opd_capacity_observe",
+    "opd_pack_first_fit",
     "opd_stream_probe",
     "opd_set_spin_limit",
     "opd_status_string",
@@ -79,6 +82,14 @@ def load_library(require_torch_runtime: bool = True) -> ctypes.CDLL:
         lib.opd_read_flags.argtypes = [vp, sz, i32, ctypes.POINTER(ctypes.c_uint32), vp]
         lib.opd_length_head_loss.restype = i32
         lib.opd_length_head_loss.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.opd_capacity_init.restype = i32
+        lib.opd_capacity_init.argtypes = [ctypes.POINTER(OpdCapacity), ctypes.c_double]
+        lib.opd_capacity_observe.restype = i32
+        lib.opd_capacity_observe.argtypes = [ctypes.POINTER(OpdCapacity), ctypes.c_double,
+                                             ctypes.POINTER(ctypes.c_int64)]
+        lib.opd_pack_first_fit.restype = i32
+        lib.opd_pack_first_fit.argtypes = [vp, i32, i64, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int32),
+                                           ctypes.POINTER(ctypes.c_int64)]
         lib.opd_stream_probe.restype = i32
         lib.opd_stream_probe.argtypes = [vp, vp, vp, sz, vp]
         lib.opd_set_spin_limit.restype = None
@@ -201,6 +212,51 @@ def length_head_loss(target_top1, draft_top1, offsets, head_logit, grad=None, ws
         out["label"].data_ptr(), out["loss"].data_ptr(), out["dlogit"].data_ptr(), ws.data_ptr(), ws.numel(),
         _stream(dev)))
     return out
+
+
+class OpdCapacity(ctypes.Structure):
+    _fields_ = [("ema", ctypes.c_double), ("beta", ctypes.c_double), ("n_obs", ctypes.c_int32)]
+
+
+class CapacityEstimate:
+    """EMA of the verification capacity (rows) observed per round; observe() returns the next budget."""
+
+    def __init__(self, beta: float):
+        self._lib = load_library(require_torch_runtime=False)
+        self._c = OpdCapacity()
+        _check("opd_capacity_init", self._lib.opd_capacity_init(ctypes.byref(self._c), float(beta)))
+
+    @property
+    def estimate(self) -> float:
+        return float(self._c.ema)
+
+    def observe(self, observed_rows: float) -> int:
+        budget = ctypes.c_int64(0)
+        _check("opd_capacity_observe", self._lib.opd_capacity_observe(ctypes.byref(self._c), float(observed_rows),
+                                                                      ctypes.byref(budget)))
+        return int(budget.value)
+
+
+def pack_first_fit(lengths, budget_rows: int, max_requests: int = 0) -> dict:
+    """First-fit packing in arrival order (host). lengths: sequence of ints >= 1.
+
+    Returns selected (int32 indices), offsets (int32, len(selected) + 1), lengths (int32) and rows.
+    """
+    import numpy as np
+
+    lib = load_library(require_torch_runtime=False)
+    ln = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+    n = int(ln.size)
+    sel = np.empty(max(n, 1), dtype=np.int32)
+    off = np.empty(n + 1, dtype=np.int32)
+    pl = np.empty(max(n, 1), dtype=np.int32)
+    n_sel = ctypes.c_int32(0)
+    rows = ctypes.c_int64(0)
+    _check("opd_pack_first_fit", lib.opd_pack_first_fit(
+        ln.ctypes.data if n else None, n, int(budget_rows), int(max_requests), sel.ctypes.data, off.ctypes.data,
+        pl.ctypes.data, ctypes.byref(n_sel), ctypes.byref(rows)))
+    k = int(n_sel.value)
+    return {"selected": sel[:k].copy(), "offsets": off[: k + 1].copy(), "lengths": pl[:k].copy(), "rows": int(rows.value)}
 
 
 def stream_probe(a, b, c) -> None:

@@ -231,6 +231,10 @@ opd_status_t run_accept(const opd_blocks_t* blocks, int64_t n_rows, const int32_
 
 }  // namespace
 
+namespace opd {
+opd_status_t record_error(opd_status_t s, const char* msg) { return fail(s, msg); }
+}  // namespace opd
+
 extern "C" {
 
 size_t opd_workspace_size(void) { return opd::kWorkspaceBytes; }

@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "opd.h"
+
 namespace opd {
 
 constexpr int kThreads = 256;  // workgroup size of every row kernel (4 wave64)
@@ -105,5 +107,8 @@ hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, size_t count, hipStream_t s);
 hipError_t launch_stream_probe(const void* a, const void* b, void* c, size_t n_vec, hipStream_t s);
 hipError_t launch_length_head(const LengthHeadParams& p, hipStream_t s);  // opd_epilogue.hip
+
+// Records the detail text returned by opd_last_error() on this thread (opd_api.cpp).
+opd_status_t record_error(opd_status_t s, const char* msg);
 
 }  // namespace opd

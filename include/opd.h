@@ -163,6 +163,39 @@ opd_status_t opd_length_head_loss(const int32_t* target_top1, const int32_t* dra
                                   const float* grad, int32_t* accept_full, float* label, float* loss,
                                   float* dlogit, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Host-side batch scheduling ("AdaFlash: Adaptive Speculative Decoding with Online Self-Improvement
+ * for High-Concurrency LLM Inference", section "Infrastructure: Async Training & Variable-Length
+ * Batching": requests with different predicted verification lengths are packed into compact batches
+ * and an exponential moving average estimates the next round's capacity). These run on the host and
+ * take HOST pointers; their output (offsets, lengths) is the packed layout the calls above take.
+ *
+ * Capacity estimate: e <- beta e + (1 - beta) observed, the first observation initialising e; the
+ * next batch's row budget is floor(e). `observed_rows` is the verification capacity (rows) the
+ * caller measured in the round just finished (e.g. what fitted in its memory budget).
+ * Errors: OPD_ERR_NULL, OPD_ERR_PARAM (beta outside [0, 1], observed negative or not finite).
+ */
+typedef struct {
+  double ema;     /* current estimate (rows) */
+  double beta;    /* weight of the previous estimate */
+  int32_t n_obs;  /* observations so far */
+} opd_capacity_t;
+opd_status_t opd_capacity_init(opd_capacity_t* c, double beta);
+opd_status_t opd_capacity_observe(opd_capacity_t* c, double observed_rows, int64_t* budget_rows);
+
+/*
+ * First-fit packing in arrival order: scans lengths[0 .. n_pending) (predicted verification rows of
+ * the pending requests, each >= 1), takes every request that still fits in budget_rows (and, if
+ * max_requests > 0, stops after max_requests), and leaves the rest queued.
+ *   selected[n_pending] out: indices of the packed requests, in arrival order (first *n_selected);
+ *   offsets[n_pending + 1] out: exclusive prefix sum of their lengths (first *n_selected + 1);
+ *   packed_lengths[n_pending] out: their lengths; *n_rows out: total rows (<= budget_rows).
+ * Errors: OPD_ERR_NULL, OPD_ERR_SHAPE (negative sizes), OPD_ERR_PARAM (a length < 1).
+ */
+opd_status_t opd_pack_first_fit(const int32_t* lengths, int32_t n_pending, int64_t budget_rows,
+                                int32_t max_requests, int32_t* selected, int32_t* offsets,
+                                int32_t* packed_lengths, int32_t* n_selected, int64_t* n_rows);
+
 /* Reads the sticky device flag word of a workspace (synchronises `stream`); clears it when
  * `clear` is non-zero. Errors: OPD_ERR_NULL, OPD_ERR_WORKSPACE, OPD_ERR_HIP. */
 opd_status_t opd_read_flags(void* ws, size_t ws_bytes, int clear, uint32_t* flags, hipStream_t stream);

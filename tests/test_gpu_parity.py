@@ -522,3 +522,40 @@ def test_length_head_on_fused_packed_batch(lib):
     _check_length_head(res, ref)
     # the uncapped prefix bounds the L-capped accept length from above
     assert np.all(res["accept_full"].cpu().numpy() >= out["accept_len"].cpu().numpy())
+
+
+# ------------------------------------------------------------------ packer -> verify
+
+
+def test_packed_batch_from_the_packer_verifies(lib):
+    """Requests packed by the host packer (first fit under an EMA budget) run through the fused call;
+    accept lengths and top-1s must match the oracle on the packed layout."""
+    import torch
+
+    rng = np.random.default_rng(31)
+    est = lib.CapacityEstimate(0.8)
+    budget = 0
+    for obs in [900.0, 700.0, 800.0]:
+        budget = est.observe(obs)
+    pending = rng.integers(1, 17, 200)
+    packed = lib.pack_first_fit(pending, budget, max_requests=64)
+    off = packed["offsets"]
+    n = int(off[-1])
+    assert n == packed["rows"] <= budget and len(packed["selected"]) <= 64
+    v = 2048
+    y = rng.normal(0, 3, (n, v)).astype(np.float32)
+    z = y + rng.normal(0, 0.7, (n, v)).astype(np.float32)
+    zt, zx = _to_dev_padded(z, v, "bf16")
+    yt, yx = _to_dev_padded(y, v, "bf16")
+    lens_pred = packed["lengths"].astype(np.int32)
+    cap = np.maximum(lens_pred - rng.integers(0, 3, lens_pred.size), 0).astype(np.int32)  # verify budgets
+    _say(f"packer -> fused: {len(lens_pred)} requests, {n} rows, budget {budget}")
+    out = lib.opd_fused_fwd_bwd_verify(zt, yt, torch.from_numpy(off).cuda(), torch.from_numpy(cap).cuda(), 0.5, 0.05)
+    torch.cuda.synchronize()
+    assert lib.read_flags(clear=True) == 0
+    d_ref, a_ref = O.top1_rows(zx), O.top1_rows(yx)
+    assert np.array_equal(out["draft_top1"].cpu().numpy(), d_ref)
+    assert np.array_equal(out["target_top1"].cpu().numpy(), a_ref)
+    acc_ref, fl = O.accept_lengths(d_ref, a_ref, off, cap)
+    assert fl == 0
+    assert np.array_equal(out["accept_len"].cpu().numpy(), acc_ref)
