@@ -529,6 +529,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
   // workgroups per CU (more resident teams hide the exchange waits). Each lane only ever reads back
   // its own 16 bytes.
   __shared__ uint4 ylds[K * kThreads];
+  __shared__ VecMax<EPV> vmlds[K * kThreads];  // per-vector maxima from phase A to phase B
   const int tid = thread_id();
   const int wave = tid >> 6;
   const int b = block_id_x();
@@ -607,9 +608,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
     }
 
     // ---- phase A
-    VecMax<EPV> vm[K];
+    float lzmax = kNegInf;
     float ek[K], bk[K];
     float lymax = kNegInf, sy = 0.f, ref_y = 0.f;
+    int kym = 0;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       opaque(zr[k]);
@@ -617,6 +619,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
       In::decode(zr[k], x);
       In::decode(ylds[k * kThreads + lt], w);
       const float ym = vmax<EPV>(w);
+      kym = (k == 0 || ym > lymax) ? k : kym;  // first slot holding the lane's maximum of y
       lymax = fmaxf(lymax, ym);
       if constexpr (kSums) {
         if (k == 0) ref_y = ym * kLog2e;
@@ -628,7 +631,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
 #pragma unroll
       for (int e = 0; e < EPV; ++e) d[e] = x[e] - w[e];
       const float zmax = vmax<EPV>(x);
-      vm[k].set(zmax, vmax<EPV>(d));
+      {
+        VecMax<EPV> vk;
+        vk.set(zmax, vmax<EPV>(d));
+        vmlds[k * kThreads + lt] = vk;  // kept in LDS until phase B (registers are the scarce resource)
+      }
+      lzmax = fmaxf(lzmax, zmax);
       if constexpr (kSums) {
         const float cz = zmax * kLog2e;
         float ez = exp2_fast(__builtin_fmaf(x[0], kLog2e, -cz));
@@ -643,12 +651,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
         bk[k] = sb;
         fence_vals(ek[k], bk[k], sy);
       }
-      vm[k].fence();
+      fence_vals(lzmax);
       fence_vals(lymax);
     }
-    float lzmax = vm[0].z();
-#pragma unroll
-    for (int k = 1; k < K; ++k) lzmax = fmaxf(lzmax, vm[k].z());
     if constexpr (kSums) {
       // the y sum is relative to the first vector's maximum: redo it from the ln maximum where y
       // rose so far above it that the terms could approach the fp32 range (rare)
@@ -670,6 +675,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
     }
 
     // ---- chunk maxima
+    // From here to the end of the first exchange this team's row is on the critical path of all
+    // K work-groups of the team: the waves take a higher issue priority than the streaming
+    // phases of the other work-groups sharing the CU, and drop it once the row constants arrive.
+    __builtin_amdgcn_s_setprio(2);
     {
       const float a = wmax(lzmax), c = wmax(lymax);
       if (ln == 0) {
@@ -685,9 +694,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
     float wsz = 0.f, wsy = 0.f;
     if constexpr (kSums) {
       const float cMz = Mzc * kLog2e, cMy = Myc * kLog2e;
-      float lsz = ek[0] * exp2_fast(vm[0].z() * kLog2e - cMz);
+      float lsz = ek[0] * exp2_fast(vmlds[lt].z() * kLog2e - cMz);
 #pragma unroll
-      for (int k = 1; k < K; ++k) lsz = __builtin_fmaf(ek[k], exp2_fast(vm[k].z() * kLog2e - cMz), lsz);
+      for (int k = 1; k < K; ++k)
+        lsz = __builtin_fmaf(ek[k], exp2_fast(vmlds[k * kThreads + lt].z() * kLog2e - cMz), lsz);
       wsz = wsum(lsz);
       wsy = wsum(sy * exp2_fast(ref_y - cMy));
     }
@@ -698,7 +708,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
       if (__builtin_amdgcn_ballot_w64(hz)) {  // a wave holding the chunk maximum of z
         int kk = K;
 #pragma unroll
-        for (int k = K - 1; k >= 0; --k) kk = (vm[k].z() == Mzc) ? k : kk;
+        for (int k = K - 1; k >= 0; --k) kk = (vmlds[k * kThreads + lt].z() == Mzc) ? k : kk;
         int iz = kBig;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -714,13 +724,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
       }
       const bool hy = lymax == Myc;
       if (__builtin_amdgcn_ballot_w64(hy)) {
-        int kk = K;
-#pragma unroll
-        for (int k = K - 1; k >= 0; --k) {
-          float w[EPV];
-          In::decode(ylds[k * kThreads + lt], w);
-          kk = (hy && vmax<EPV>(w) == Myc) ? k : kk;
-        }
+        const int kk = kym;
         int iy = kBig;
         float za = 0.f;
 #pragma unroll
@@ -843,6 +847,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
       }
     }
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
     if (sh.err) break;
 
     const float Mz = sh.row[z0 + kRowMz];
@@ -860,13 +865,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
       rc.init(Mz, ln_sz, delta);
 
       // ---- phase B: vectors that pass the bound use their phase-A sums, the rest (near the peak)
-      // are summed element by element
+      // are summed element by element. Phase B feeds the second exchange: it runs above the
+      // streaming priority, and the reduction and exchange above that.
+      __builtin_amdgcn_s_setprio(1);
       float pe = 0.f, pb = 0.f, s_slow = 0.f, r_slow = 0.f;
       uint32_t slowbits = 0;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const float sc = vector_scale(rc, vm[k].z());
-        const bool slow = vector_may_clip(rc, sc, vm[k].d(), tau_b);
+        const VecMax<EPV> vk = vmlds[k * kThreads + lt];
+        const float sc = vector_scale(rc, vk.z());
+        const bool slow = vector_may_clip(rc, sc, vk.d(), tau_b);
         slowbits |= (uint32_t)slow << k;
         const float u = slow ? 0.f : sc;
         pe = __builtin_fmaf(u, ek[k], pe);
@@ -890,6 +898,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
           fence_vals(r_slow, s_slow);
         }
       }
+      __builtin_amdgcn_s_setprio(2);
       {
         const float a = wsum(__builtin_fmaf(1.f - delta, pe, pb) + s_slow);
         const float c = wsum(__builtin_fmaf(-delta, pe, pb) + r_slow);
@@ -943,6 +952,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
         }
       }
       __syncthreads();
+      __builtin_amdgcn_s_setprio(0);
       if (sh.err) break;
 
       if constexpr (MODE == kFused) {
