@@ -13,7 +13,9 @@ HBM. Prints one JSON line:
   its stream over K launches without verification; achieved = algorithmic bytes per launch
   (read z and y once, write dz once, plus 44 bytes of per-row outputs) / average launch time,
   against the MI355X HBM peak of 8 TB/s. measured_stream_gbs: the library's stream probe (the same
-  two-reads-one-write pattern over the same buffers, no arithmetic), timed the same way. traffic = HBM bytes per launch from the rocprofv3
+  two-reads-one-write pattern over the same buffers, no arithmetic), timed the same way;
+  measured_read_only_gbs / measured_write_only_gbs: the probe's read-only and write-only modes over
+  the same buffers (the ceilings of the two halves of the pattern). traffic = HBM bytes per launch from the rocprofv3
   FETCH_SIZE / WRITE_SIZE counters recorded in profiles/ for the current kernel source (null if the
   kernel changed since they were taken).
 * cpu_baseline: the float64 oracle (loss, gradient, top-1s, accept lengths) on a bounded sample of
@@ -217,22 +219,28 @@ def main():
         sys.exit(1)
 
     # achievable bandwidth of the same traffic pattern (read z and y, write a dz-sized buffer) with
-    # no arithmetic: the stream probe of the library, timed the same way
-    stream_gbs = None
+    # no arithmetic: the stream probe of the library, timed the same way; then the read-only and
+    # write-only ceilings over the same buffers
+    stream_gbs = read_only_gbs = write_only_gbs = None
     if not args.profile:
         zb = z.contiguous().view(torch.uint8).view(-1)
         yb = y.contiguous().view(torch.uint8).view(-1)
         dzb = out["dz"].view(torch.uint8).view(-1)
         if dzb.numel() != zb.numel():
             dzb = torch.empty_like(zb)
-        opd.stream_probe(zb, yb, dzb)
-        ev0.record(stream)
-        for _ in range(args.steps):
-            opd.stream_probe(zb, yb, dzb)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        probe_ms = ev0.elapsed_time(ev1) / args.steps
-        stream_gbs = 3 * zb.numel() / (probe_ms * 1e-3) / 1e9
+
+        def probe_gbs(a, b, c, streams):
+            opd.stream_probe(a, b, c)
+            ev0.record(stream)
+            for _ in range(args.steps):
+                opd.stream_probe(a, b, c)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            return streams * zb.numel() / (ev0.elapsed_time(ev1) / args.steps * 1e-3) / 1e9
+
+        stream_gbs = probe_gbs(zb, yb, dzb, 3)
+        read_only_gbs = probe_gbs(zb, yb, None, 2)
+        write_only_gbs = probe_gbs(None, None, dzb, 1)
         del zb, yb, dzb
 
     # length-head epilogue (a separate small kernel) on this step's top-1s, one logit per block
@@ -307,6 +315,8 @@ def main():
             # bandwidth for this traffic pattern on this device, and the kernel's share of it
             "measured_stream_gbs": stream_gbs,
             "frac_of_measured_stream": (achieved / stream_gbs) if stream_gbs else None,
+            "measured_read_only_gbs": read_only_gbs,
+            "measured_write_only_gbs": write_only_gbs,
         },
         "cpu_baseline": cpu,
         # next-row pieces timed beside the step (not part of it): the length-head epilogue per launch

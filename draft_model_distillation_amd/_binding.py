@@ -260,15 +260,22 @@ def pack_first_fit(lengths, budget_rows: int, max_requests: int = 0) -> dict:
 
 
 def stream_probe(a, b, c) -> None:
-    """c = a XOR b over the bytes of three equally sized, 16-byte aligned device tensors (bandwidth probe)."""
+    """c = a XOR b over the bytes of equally sized, 16-byte aligned device tensors (bandwidth probe).
+
+    c=None only reads a and b; a=b=None only writes c.
+    """
     lib = load_library()
-    nbytes = a.numel() * a.element_size()
-    if b.numel() * b.element_size() != nbytes or c.numel() * c.element_size() != nbytes:
-        raise ValueError("a, b and c must hold the same number of bytes")
-    if not (a.is_contiguous() and b.is_contiguous() and c.is_contiguous()):
-        raise ValueError("a, b and c must be contiguous")
-    _check("opd_stream_probe", lib.opd_stream_probe(a.data_ptr(), b.data_ptr(), c.data_ptr(), ctypes.c_size_t(nbytes),
-                                                    _stream(a.device)))
+    given = [t for t in (a, b, c) if t is not None]
+    if (a is None) != (b is None) or not given:
+        raise ValueError("a and b must be both given or both None, and something must be streamed")
+    nbytes = given[0].numel() * given[0].element_size()
+    if any(t.numel() * t.element_size() != nbytes for t in given):
+        raise ValueError("the tensors must hold the same number of bytes")
+    if not all(t.is_contiguous() for t in given):
+        raise ValueError("the tensors must be contiguous")
+    ptr = [0 if t is None else t.data_ptr() for t in (a, b, c)]
+    _check("opd_stream_probe", lib.opd_stream_probe(ptr[0], ptr[1], ptr[2], ctypes.c_size_t(nbytes),
+                                                    _stream(given[0].device)))
 
 
 def _blocks(offsets, lengths):

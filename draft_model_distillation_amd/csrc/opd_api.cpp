@@ -387,7 +387,8 @@ opd_status_t opd_read_flags(void* ws, size_t ws_bytes, int clear, uint32_t* flag
 
 opd_status_t opd_stream_probe(const void* a, const void* b, void* c, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return OPD_OK;
-  if (!a || !b || !c) return fail(OPD_ERR_NULL, "a, b and c must be non-NULL");
+  if (!a != !b) return fail(OPD_ERR_NULL, "a and b must be both given or both NULL");
+  if (!a && !c) return fail(OPD_ERR_NULL, "nothing to stream: a, b and c are NULL");
   if (bytes % 16) return fail(OPD_ERR_SHAPE, "bytes must be a multiple of 16");
   if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) | reinterpret_cast<uintptr_t>(c)) % 16)
     return fail(OPD_ERR_ALIGN, "buffers must be 16-byte aligned");

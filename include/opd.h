@@ -203,9 +203,14 @@ opd_status_t opd_read_flags(void* ws, size_t ws_bytes, int clear, uint32_t* flag
 /* Measurement aid, not part of the method: streams the HBM traffic pattern of the fused path --
  * two 16-byte reads and one 16-byte write per vector, nontemporal -- with no arithmetic beyond
  * c = a XOR b, so that its rate is the achievable bandwidth for that pattern on this device.
- *   a, b   device buffers of `bytes` bytes (read); c device buffer of `bytes` bytes (written).
- *   bytes  multiple of 16; the three pointers 16-byte aligned; 0 is a no-op.
- * Errors: OPD_ERR_NULL, OPD_ERR_SHAPE (bytes not a multiple of 16), OPD_ERR_ALIGN, OPD_ERR_HIP. */
+ * With c NULL it only reads a and b; with a and b both NULL it only writes c: the read-only and
+ * write-only ceilings of the same device.
+ *   a, b   device buffers of `bytes` bytes (read), both given or both NULL.
+ *   c      device buffer of `bytes` bytes (written), or NULL; at least one of (a, b) and c is given.
+ *          In read-only mode c is NULL and nothing is written.
+ *   bytes  multiple of 16; the given pointers 16-byte aligned; 0 is a no-op.
+ * Errors: OPD_ERR_NULL (exactly one of a, b given, or nothing to do), OPD_ERR_SHAPE (bytes not a
+ * multiple of 16), OPD_ERR_ALIGN, OPD_ERR_HIP. */
 opd_status_t opd_stream_probe(const void* a, const void* b, void* c, size_t bytes, hipStream_t stream);
 
 /* Debug knob for tests of the failure path: caps every cross-workgroup wait at `spins` polls

@@ -111,7 +111,9 @@ def test_infinite_tau_is_a_valid_parameter(lib):
 
 def test_stream_probe_validation(lib):
     # checked before any HIP call: NULL buffers, a size that is not whole 16-byte vectors, misalignment
-    assert lib.opd_stream_probe(None, P, P, 64, None) == 1
+    assert lib.opd_stream_probe(None, P, P, 64, None) == 1  # only one of a, b
+    assert lib.opd_stream_probe(P, None, None, 64, None) == 1
+    assert lib.opd_stream_probe(None, None, None, 64, None) == 1  # nothing to stream
     assert lib.opd_stream_probe(P, P, P, 40, None) == 2
     assert lib.opd_stream_probe(P, P + 8, P, 64, None) == 4
     assert lib.opd_stream_probe(None, None, None, 0, None) == 0

@@ -432,6 +432,17 @@ def test_stream_probe_xor(lib):
     torch.cuda.synchronize()
     assert torch.equal(cd[:n].cpu(), a ^ b)
     assert torch.all(cd[n:] == 7)
+    # read-only mode writes nothing; write-only mode writes every vector of c and nothing past it
+    _say("stream probe read-only / write-only")
+    lib.stream_probe(ad, bd, None)
+    torch.cuda.synchronize()
+    assert torch.equal(cd[:n].cpu(), a ^ b)
+    lib.stream_probe(None, None, cd[:n])
+    torch.cuda.synchronize()
+    got = cd[:n].cpu().view(torch.int64).view(-1, 2)
+    idx = torch.arange(n // 16, dtype=torch.int64)
+    assert torch.equal(got[:, 0], idx) and torch.all(got[:, 1] == 0)
+    assert torch.all(cd[n:] == 7)
 
 
 # ------------------------------------------------------------------ length-head epilogue
