@@ -3,7 +3,7 @@
 The computation lives in hand-written gfx950 HIP kernels behind the C ABI of include/opd.h
 (libopd_mi355x.so, built by ``draft_model_distillation_amd.build``). This package only binds it:
 
-    opd_loss_fwd, opd_loss_bwd, verify_accept_len, opd_fused_fwd_bwd_verify
+    opd_loss_fwd, opd_loss_bwd, verify_accept_len, opd_fused_fwd_bwd_verify, verify_sample
 
 take torch device tensors and enqueue on torch's current stream.
 """
@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     OPD_BF16,
     OPD_F32,
     OPD_FLAG_BAD_OFFSETS,
+    OPD_FLAG_BAD_TOKEN,
     OPD_FLAG_NEG_L,
     OPD_FLAG_SPIN_TIMEOUT,
     OpdError,
@@ -28,5 +29,6 @@ from ._binding import (  # noqa: F401
     set_spin_limit,
     stream_probe,
     verify_accept_len,
+    verify_sample,
     workspace,
 )

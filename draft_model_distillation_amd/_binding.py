@@ -19,6 +19,7 @@ OPD_BF16 = 1
 OPD_FLAG_NEG_L = 1
 OPD_FLAG_BAD_OFFSETS = 2
 OPD_FLAG_SPIN_TIMEOUT = 4
+OPD_FLAG_BAD_TOKEN = 8
 
 EXPORTED_SYMBOLS = (
     "opd_workspace_size",
@@ -28,6 +29,7 @@ EXPORTED_SYMBOLS = (
     "opd_fused_fwd_bwd_verify",
     "opd_read_flags",
     "opd_length_head_loss",
+    "opd_verify_sample",
     "opd_capacity_init",
     "opd_capacity_observe",
     "opd_pack_first_fit",
@@ -90,6 +92,9 @@ def load_library(require_torch_runtime: bool = True) -> ctypes.CDLL:
         lib.opd_pack_first_fit.restype = i32
         lib.opd_pack_first_fit.argtypes = [vp, i32, i64, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_int64)]
+        lib.opd_verify_sample.restype = i32
+        lib.opd_verify_sample.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(OpdBlocks), vp, vp, vp,
+                                          ctypes.c_float, vp, vp, vp, vp, sz, vp]
         lib.opd_stream_probe.restype = i32
         lib.opd_stream_probe.argtypes = [vp, vp, vp, sz, vp]
         lib.opd_set_spin_limit.restype = None
@@ -343,6 +348,43 @@ def verify_accept_len(z, y, offsets, lengths, ws=None):
                                _stream(dev))
     _check("verify_accept_len", st)
     return a, d, acc
+
+
+def verify_sample(z, y, offsets, lengths, draft_tokens, u_accept, u_resample, temperature: float, ws=None,
+                  out=None):
+    """Speculative-sampling verification at a temperature (opd_verify_sample).
+
+    Returns a dict: accept_len [B] i32, token [B] i32 (-1 when none), row_lse [R, 4] f32 (reference and
+    log2 of the sum of 2^(x log2(e) / T) for z, then for y). ``out`` may hold preallocated tensors under
+    the same keys.
+    """
+    torch = _torch()
+    lib = load_library()
+    zp, rows, vocab, ld = _matrix(z, "z")
+    yp, rows_y, vocab_y, ld_y = _matrix(y, "y")
+    if (rows, vocab, ld) != (rows_y, vocab_y, ld_y) or z.dtype != y.dtype:
+        raise ValueError("z and y must have the same shape, row pitch and dtype")
+    dev = z.device
+    ws = workspace(dev) if ws is None else ws
+    blocks = _blocks(offsets, lengths)
+    if blocks is None or lengths is None:
+        raise ValueError("offsets and L are required")
+    for name, t, n, dt in (("draft_tokens", draft_tokens, rows, torch.int32), ("u_accept", u_accept, rows, torch.float32),
+                           ("u_resample", u_resample, blocks.n_blocks, torch.float32)):
+        if t.dtype != dt or t.numel() != n or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of {n} elements on {dev}")
+    o = dict(out) if out is not None else {}
+    if "accept_len" not in o:
+        o["accept_len"] = torch.empty(blocks.n_blocks, dtype=torch.int32, device=dev)
+        o["token"] = torch.empty(blocks.n_blocks, dtype=torch.int32, device=dev)
+        o["row_lse"] = torch.empty(rows, 4, dtype=torch.float32, device=dev)
+    st = lib.opd_verify_sample(zp, yp, _dtype_code(z), rows, vocab, ld, ctypes.byref(blocks), draft_tokens.data_ptr(),
+                               u_accept.data_ptr(), u_resample.data_ptr(), float(temperature),
+                               _ptr(o["accept_len"]) if blocks.n_blocks else None,
+                               _ptr(o["token"]) if blocks.n_blocks else None, o["row_lse"].data_ptr(),
+                               ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("opd_verify_sample", st)
+    return o
 
 
 def opd_fused_fwd_bwd_verify(z, y, offsets, lengths, alpha: float, tau: float, grad_loss=None, dz_dtype=None,

@@ -19,6 +19,7 @@
 static_assert(OPD_FLAG_NEG_L == opd::kFlagNegL, "flag mismatch");
 static_assert(OPD_FLAG_BAD_OFFSETS == opd::kFlagBadOffsets, "flag mismatch");
 static_assert(OPD_FLAG_SPIN_TIMEOUT == opd::kFlagSpinTimeout, "flag mismatch");
+static_assert(OPD_FLAG_BAD_TOKEN == opd::kFlagBadToken, "flag mismatch");
 
 namespace {
 
@@ -363,6 +364,49 @@ opd_status_t opd_length_head_loss(const int32_t* target_top1, const int32_t* dra
   p.flags = static_cast<uint32_t*>(ws);
   hipError_t e = opd::launch_length_head(p, stream);
   if (e != hipSuccess) return hip_fail(e, "length-head kernel launch");
+  return OPD_OK;
+}
+
+opd_status_t opd_verify_sample(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+                               int64_t ld, const opd_blocks_t* blocks, const int32_t* draft_tokens,
+                               const float* u_accept, const float* u_resample, float temperature,
+                               int32_t* accept_len, int32_t* out_token, float* row_lse, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  opd_status_t s = check_logits(z, y, dt, n_rows, vocab, ld);
+  if (s != OPD_OK) return s;
+  if ((s = check_blocks(blocks, true)) != OPD_OK) return s;
+  if (!(temperature > 0.f) || std::isinf(temperature))
+    return fail(OPD_ERR_PARAM, "temperature must be positive and finite");
+  // fp32 must hold log2(e) / T (and scaled logits of |z| <= 1e4) without overflow
+  if (temperature < 1e-6f) return fail(OPD_ERR_PARAM, "temperature must be >= 1e-6");
+  if (n_rows > 0 && (!draft_tokens || !u_accept || !row_lse))
+    return fail(OPD_ERR_NULL, "draft_tokens, u_accept and row_lse must be non-NULL");
+  if (blocks->n_blocks > 0 && (!u_resample || !accept_len || !out_token))
+    return fail(OPD_ERR_NULL, "u_resample, accept_len and out_token must be non-NULL");
+  if ((s = check_ws(ws, ws_bytes)) != OPD_OK) return s;
+  if (n_rows == 0 && blocks->n_blocks == 0) return OPD_OK;
+  const int in_bf16 = dt == OPD_BF16;
+  const int epv = in_bf16 ? 8 : 4;
+  opd::SampleParams p;
+  p.z = static_cast<const uint8_t*>(z);
+  p.y = static_cast<const uint8_t*>(y);
+  p.ld_bytes = ld * (int64_t)dtype_size(dt);
+  p.vocab = (int32_t)vocab;
+  p.nvec = (int32_t)((vocab + epv - 1) / epv);
+  p.n_rows = (int32_t)n_rows;
+  p.n_blocks = blocks->n_blocks;
+  p.c = (float)(1.4426950408889634 / (double)temperature);
+  p.offsets = blocks->offsets;
+  p.L = blocks->L;
+  p.draft = draft_tokens;
+  p.u_accept = u_accept;
+  p.u_resample = u_resample;
+  p.stats = row_lse;
+  p.accept_len = accept_len;
+  p.token = out_token;
+  p.flags = static_cast<uint32_t*>(ws);
+  hipError_t e = opd::launch_sample_verify(p, in_bf16, stream);
+  if (e != hipSuccess) return hip_fail(e, "sampling-verify kernel launch");
   return OPD_OK;
 }
 

@@ -24,6 +24,7 @@ constexpr size_t kWorkspaceBytes = kHeaderBytes + (size_t)kMaxGrid * kUnitBytesP
 constexpr uint32_t kFlagNegL = 1u;
 constexpr uint32_t kFlagBadOffsets = 2u;
 constexpr uint32_t kFlagSpinTimeout = 4u;
+constexpr uint32_t kFlagBadToken = 8u;
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 constexpr int kMaxTeamSize = 128;
 
@@ -98,6 +99,28 @@ struct LengthHeadParams {
   uint32_t* flags;
 };
 
+// Speculative-sampling verification at temperature T (opd_sample.hip).
+constexpr int kMaxSampleTiles = 2048;  // 64-vector tiles of the widest row (524288 fp32 logits)
+struct SampleParams {
+  const uint8_t* z;
+  const uint8_t* y;
+  int64_t ld_bytes;
+  int32_t vocab;
+  int32_t nvec;  // 16-byte vectors per row covering vocab
+  int32_t n_rows;
+  int32_t n_blocks;
+  float c;  // log2(e) / T
+  const int32_t* offsets;
+  const int32_t* L;
+  const int32_t* draft;
+  const float* u_accept;
+  const float* u_resample;
+  float* stats;  // [n_rows][4]: reference and log2 of the sum for z / T, then for y / T
+  int32_t* accept_len;
+  int32_t* token;
+  uint32_t* flags;
+};
+
 // in_bf16: 1 if z/y are bf16 (else fp32); out_bf16: 1 if dz is bf16 (else fp32); K: slots/thread.
 hipError_t launch_team(const TeamParams& p, int mode, int in_bf16, int out_bf16, int K, int grid,
                        hipStream_t s);
@@ -107,6 +130,7 @@ hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, size_t count, hipStream_t s);
 hipError_t launch_stream_probe(const void* a, const void* b, void* c, size_t n_vec, hipStream_t s);
 hipError_t launch_length_head(const LengthHeadParams& p, hipStream_t s);  // opd_epilogue.hip
+hipError_t launch_sample_verify(const SampleParams& p, int in_bf16, hipStream_t s);  // opd_sample.hip
 
 // Records the detail text returned by opd_last_error() on this thread (opd_api.cpp).
 opd_status_t record_error(opd_status_t s, const char* msg);

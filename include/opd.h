@@ -71,6 +71,7 @@ typedef enum {
 #define OPD_FLAG_NEG_L 1u        /* some block had L < 0 (treated as 0)                         */
 #define OPD_FLAG_BAD_OFFSETS 2u  /* some block had decreasing / out-of-range offsets (accept 0)   */
 #define OPD_FLAG_SPIN_TIMEOUT 4u /* a cross-workgroup wait exceeded its bound: outputs invalid    */
+#define OPD_FLAG_BAD_TOKEN 8u    /* a verified row proposed a token outside [0, vocab) (rejected)  */
 
 /* Packed verification blocks ("Infrastructure: ... Variable-Length Batching"): block b owns rows
  * offsets[b] .. offsets[b+1]-1; L[b] is the length head's predicted verification length.
@@ -162,6 +163,43 @@ opd_status_t opd_length_head_loss(const int32_t* target_top1, const int32_t* dra
                                   const int32_t* offsets, int32_t n_blocks, const float* head_logit,
                                   const float* grad, int32_t* accept_full, float* label, float* loss,
                                   float* dlogit, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Stochastic verification at a sampling temperature (speculative sampling). The pages name the
+ * temperature as a parameter to tune when drafter and target are combined ("AdaFlash: Adaptive
+ * Speculative Decoding via On-Policy Distilled Diffusion Drafters", skills directory page, section
+ * "Implementation Steps") but give no rule for it; the rule is the published speculative-sampling
+ * one (Leviathan et al. 2023; Chen et al. 2023). With p_r = softmax(z_r / T), q_r = softmax(y_r / T)
+ * and x_r = draft_tokens[r], per packed block b (rows s = offsets[b] .. offsets[b+1]-1, n_b rows,
+ * n = clamp(L[b], 0, n_b)):
+ *   - rows s .. s+n-1 are verified in order; row r's proposal is accepted when
+ *     u_accept[r] * p_r(x_r) <= q_r(x_r); accept_len[b] = rows accepted before the first rejection;
+ *   - out_token[b]: at the first rejected row r, a draw from max(0, q_r - p_r) normalised (from q_r
+ *     if that residual is zero everywhere); after n accepted rows with n < n_b, a draw from q at row
+ *     s + n; -1 when n = n_b and all were accepted, or the block is malformed. A draw from weights w
+ *     with v = u_resample[b] is the smallest index i with w_0 + ... + w_i > v * sum(w).
+ *   z, y             [n_rows, ld] logits of dtype dt (as for the other calls).
+ *   draft_tokens     [n_rows] int32: proposed tokens; one outside [0, vocab) is rejected and raises
+ *                    OPD_FLAG_BAD_TOKEN.
+ *   u_accept         [n_rows] f32 uniforms in [0, 1); u_resample [n_blocks] f32 uniforms in [0, 1).
+ *                    The random numbers are the caller's: the call draws none.
+ *   temperature      T in [1e-6, inf).
+ *   accept_len, out_token [n_blocks] int32 out.
+ *   row_lse          [n_rows][4] f32 out: (c_z, l_z, c_y, l_y) with log2 sum_v 2^(z_v log2(e) / T) =
+ *                    c_z + l_z (c_z a reference near the row maximum, l_z = log2 of the sum relative to
+ *                    it), likewise for y; so log of the normaliser of softmax(z / T) is (c_z + l_z) ln 2.
+ * Every row's row_lse is computed (one read of z and y); the decisions then read two elements per
+ * verified row, and each draw reads its row once more. Decisions and draws are taken in fp32 on sums
+ * formed in a fixed order (deterministic); a draw whose target falls on a rounding edge takes the last
+ * positive weight before it. Negative L and malformed offsets raise the greedy call's flags.
+ * Errors: OPD_ERR_NULL, OPD_ERR_SHAPE, OPD_ERR_DTYPE, OPD_ERR_ALIGN, OPD_ERR_PARAM (temperature),
+ * OPD_ERR_WORKSPACE, OPD_ERR_HIP.
+ */
+opd_status_t opd_verify_sample(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+                               int64_t ld, const opd_blocks_t* blocks, const int32_t* draft_tokens,
+                               const float* u_accept, const float* u_resample, float temperature,
+                               int32_t* accept_len, int32_t* out_token, float* row_lse, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
 
 /*
  * Host-side batch scheduling ("AdaFlash: Adaptive Speculative Decoding with Online Self-Improvement

@@ -97,6 +97,34 @@ def test_verify_and_fused_validation(lib):
                                         None, WS, 100, None) == 6
 
 
+def test_verify_sample_validation(lib):
+    ws = lib.opd_workspace_size()
+    bl = m._binding.OpdBlocks(P, P, 2)
+
+    def call(z=P, dt=BF16, n=4, v=64, ld=64, blocks=bl, draft=P, ua=P, ur=P, t=0.8, acc=P, tok=P, lse=P, wsp=WS,
+             wsb=ws):
+        b = ctypes.byref(blocks) if blocks is not None else None
+        return lib.opd_verify_sample(z, P, dt, n, v, ld, b, draft, ua, ur, t, acc, tok, lse, wsp, wsb, None)
+
+    # (a call that passes validation would launch kernels on the fake pointers: never made here)
+    assert call(z=None) == 1
+    assert call(blocks=None) == 1
+    assert call(draft=None) == 1 and call(ua=None) == 1 and call(lse=None) == 1
+    assert call(ur=None) == 1 and call(acc=None) == 1 and call(tok=None) == 1
+    assert call(blocks=m._binding.OpdBlocks(P, P, -1)) == 2
+    assert call(blocks=m._binding.OpdBlocks(None, P, 2)) == 1
+    assert call(dt=5) == 3
+    assert call(ld=60) == 2
+    assert call(z=P + 8) == 4
+    for t in (0.0, -1.0, float("nan"), float("inf"), 1e-7):
+        assert call(t=t) == 5, t
+    assert "temperature" in lib.opd_last_error().decode()
+    assert call(wsb=8) == 6
+    # nothing to do: no rows, no blocks
+    assert lib.opd_verify_sample(None, None, BF16, 0, 64, 64, ctypes.byref(m._binding.OpdBlocks(None, None, 0)),
+                                 None, None, None, 1.0, None, None, None, WS, ws, None) == 0
+
+
 def test_zero_rows_accepts_null_buffers(lib):
     ws = lib.opd_workspace_size()
     # nothing to do: no HIP call is needed and NULL data pointers are fine
