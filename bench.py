@@ -255,6 +255,27 @@ def main():
         torch.cuda.synchronize()
         head_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
 
+    # speculative-sampling verification at T = 1 over the whole workload (proposals = this step's draft
+    # top-1s, seeded uniforms): per-row log2-sums of z and y (one read of both), decisions and draws
+    sample = None
+    if not args.profile and len(lens) > 0:
+        g = torch.Generator(device="cpu").manual_seed(7)
+        ua = (torch.randint(0, 1 << 24, (n,), generator=g) / float(1 << 24)).to(torch.float32).to(dev)
+        ur = (torch.randint(0, 1 << 24, (len(lens),), generator=g) / float(1 << 24)).to(torch.float32).to(dev)
+        so = opd.verify_sample(z, y, off, lens, out["draft_top1"], ua, ur, 1.0, ws=ws)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            opd.verify_sample(z, y, off, lens, out["draft_top1"], ua, ur, 1.0, ws=ws, out=so)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        sample_ms = ev0.elapsed_time(ev1) / args.steps
+        read_bytes = 2 * n * rec.vocab * (2 if rec.dtype == "bf16" else 4)
+        sample = {"ms": sample_ms, "read_bytes": read_bytes, "gbs": read_bytes / (sample_ms * 1e-3) / 1e9,
+                  "mean_accept": float(so["accept_len"].float().mean().item())}
+        if opd.read_flags(ws, clear=True) != 0:
+            print("[bench] device flags raised by the sampling verification", file=sys.stderr)
+            sys.exit(1)
+
     # host packer: first fit of the workload's requests (their lengths, in order) under a budget
     # of half the workload's rows, per call through the binding
     lengths_np = np.diff(off.cpu().numpy())
@@ -320,9 +341,11 @@ def main():
         },
         "cpu_baseline": cpu,
         # next-row pieces timed beside the step (not part of it): the length-head epilogue per launch
-        # over this workload's blocks (includes the binding's output allocation) and the host
-        # packer per call over this workload's requests
+        # over this workload's blocks (includes the binding's output allocation), the host packer
+        # per call over this workload's requests, and the speculative-sampling verification
         "extras": {"length_head_epilogue_us": head_us, "host_packer_us": pack_us,
+                   # opd_verify_sample at T = 1 (both kernels) per call; gbs = z and y read once / time
+                   "sampling_verify": sample,
                    "packer_requests": int(lengths_np.size)},
     }
     print(json.dumps(result), flush=True)

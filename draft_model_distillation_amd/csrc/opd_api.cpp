@@ -405,6 +405,8 @@ opd_status_t opd_verify_sample(const void* z, const void* y, opd_dtype_t dt, int
   p.accept_len = accept_len;
   p.token = out_token;
   p.flags = static_cast<uint32_t*>(ws);
+  p.slices = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + opd::kHeaderBytes);
+  p.block0 = 0;
   hipError_t e = opd::launch_sample_verify(p, in_bf16, stream);
   if (e != hipSuccess) return hip_fail(e, "sampling-verify kernel launch");
   return OPD_OK;

@@ -101,6 +101,9 @@ struct LengthHeadParams {
 
 // Speculative-sampling verification at temperature T (opd_sample.hip).
 constexpr int kMaxSampleTiles = 2048;  // 64-vector tiles of the widest row (524288 fp32 logits)
+constexpr int kSampleSlices = 16;      // workgroups that sum one draw row
+// blocks per launch pair: their slice sums fill the workspace after its header
+constexpr int kSampleBatch = (int)((kWorkspaceBytes - kHeaderBytes) / (kSampleSlices * sizeof(float)));
 struct SampleParams {
   const uint8_t* z;
   const uint8_t* y;
@@ -119,6 +122,8 @@ struct SampleParams {
   int32_t* accept_len;
   int32_t* token;
   uint32_t* flags;
+  float* slices;   // workspace: [kSampleBatch][kSampleSlices] slice sums of the draw rows
+  int32_t block0;  // first block of the current batch
 };
 
 // in_bf16: 1 if z/y are bf16 (else fp32); out_bf16: 1 if dz is bf16 (else fp32); K: slots/thread.

@@ -11,18 +11,21 @@
 // Length Head for Token-Level Variance" and "Infrastructure: Async Training & Variable-Length
 // Batching".
 //
-// Two kernels:
+// Three kernels:
 //   k_row_lse_t     one workgroup per row: one streaming read of z and y (4V bytes for bf16) giving
 //                   log2 sum 2^(x log2e / T) of both rows as (reference, log2 of the sum relative to
 //                   it), with per-vector references so that no row maximum is needed first.
-//   k_sample_verify one workgroup per block: the accept decisions of its verified rows (one lane
-//                   each, two element gathers per row), then, if a token is to be drawn, the inverse
-//                   CDF of the draw row's weights in index order: wave-sized tiles of 64 vectors,
-//                   tile sums from an inclusive wave scan, a scan over lane groups of tiles to find
-//                   the tile, and the same wave scan inside that tile to find the element.
-// Draws are taken on sums formed in a fixed order, so results are deterministic; where rounding of
-// those sums leaves the target at a tile or vector edge, the last positive weight before the edge
-// is taken.
+//   k_sample_slices (block, slice) workgroups: each takes the block's accept decisions (one lane per
+//                   verified row, two element gathers each) and, if a token is to be drawn, the
+//                   weight sum of one of kSampleSlices contiguous slices of the draw row, so that the
+//                   draw row is read by many workgroups at once.
+//   k_sample_pick   one workgroup per block: the decisions again (writing accept_len), the slice
+//                   whose running sum passes u * total, the tile (64 vectors) inside it, and the
+//                   element inside the tile, each level from the same sums as the level above.
+// A tile's sum is the last value of an inclusive wave scan, a slice's the sequential sum of its tile
+// sums, the total the sequential sum of the slice sums: fixed orders, so results are deterministic;
+// where rounding leaves the target at a slice, tile or vector edge, the last positive weight before
+// the edge is taken.
 //
 // Compiled with the default IEEE mode, like the epilogue kernels.
 
@@ -223,36 +226,46 @@ __device__ __forceinline__ float wave_scan(float x, int lane) {
   return x;
 }
 
+// Sum of the weights of tile t (64 vectors, one per lane of the calling wave): the last value of
+// the inclusive wave scan, so that the search inside a tile sees exactly this total.
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads) k_sample_verify(SampleParams P) {
-  using D = Dec<BF16>;
-  constexpr int EPV = D::EPV;
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ float tile_sum[kMaxSampleTiles];
-  __shared__ int s_first;
-  __shared__ int s_tile;
-  __shared__ float s_rem;
-  __shared__ int s_idx;
+__device__ __forceinline__ float tile_total(const DrawRow& d, int t, int nvec, int vocab, int lane) {
+  constexpr int EPV = Dec<BF16>::EPV;
+  float w[EPV];
+  vector_weights<BF16>(d, t * 64 + lane, nvec, vocab, w);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) s += w[e];
+  return __shfl(wave_scan(s, lane), 63);
+}
 
+// Outcome of a block's decisions: accept length, and the row and kind of the draw (kind 0: none).
+// bad = malformed offsets. Every thread of the workgroup calls it (it synchronises).
+struct Outcome {
+  int first;
+  int row;
+  int kind;
+  bool bad;
+};
+
+template <bool BF16>
+__device__ Outcome decide(const SampleParams& P, int b, bool raise_flags, int* s_first) {
+  using D = Dec<BF16>;
+  const int tid = threadIdx.x;
+  Outcome o{0, -1, 0, false};
   const int start = P.offsets[b], end = P.offsets[b + 1];
   if (start < 0 || end < start || end > P.n_rows) {
-    if (tid == 0) {
-      atomicOr(P.flags, kFlagBadOffsets);
-      P.accept_len[b] = 0;
-      P.token[b] = -1;
-    }
-    return;
+    if (raise_flags && tid == 0) atomicOr(P.flags, kFlagBadOffsets);
+    o.bad = true;
+    return o;
   }
   const int nb = end - start;
   const int Lb = P.L[b];
-  if (Lb < 0 && tid == 0) atomicOr(P.flags, kFlagNegL);
+  if (raise_flags && Lb < 0 && tid == 0) atomicOr(P.flags, kFlagNegL);
   const int n = min(max(Lb, 0), nb);
-
-  // ---- decisions: one lane per verified row, the first rejected row wins
   int first = n;
   for (int j0 = 0; j0 < n; j0 += kThreads) {
-    if (tid == 0) s_first = 0x7fffffff;
+    if (tid == 0) *s_first = 0x7fffffff;
     __syncthreads();
     const int j = j0 + tid;
     if (j < n) {
@@ -261,7 +274,7 @@ __global__ void __launch_bounds__(kThreads) k_sample_verify(SampleParams P) {
       bool rej;
       if (x < 0 || x >= P.vocab) {
         rej = true;
-        atomicOr(P.flags, kFlagBadToken);
+        if (raise_flags) atomicOr(P.flags, kFlagBadToken);
       } else {
         const float* st = P.stats + 4 * (int64_t)r;
         const float zx = D::elem(P.z + (int64_t)r * P.ld_bytes, x);
@@ -270,154 +283,207 @@ __global__ void __launch_bounds__(kThreads) k_sample_verify(SampleParams P) {
         const float q = ex2(__builtin_fmaf(yx, P.c, -st[2]) - st[3]);
         rej = P.u_accept[r] * p > q;
       }
-      if (rej) atomicMin(&s_first, j);
+      if (rej) atomicMin(s_first, j);
     }
     __syncthreads();
-    const int f = s_first;
+    const int f = *s_first;
     __syncthreads();
     if (f != 0x7fffffff) {
       first = f;
       break;
     }
   }
-  if (tid == 0) P.accept_len[b] = first;
-
-  DrawRow d;
-  int draw_row;
+  o.first = first;
   if (first < n) {
-    draw_row = start + first;
-    d.kind = 1;
+    o.row = start + first;
+    o.kind = 1;
   } else if (n < nb) {
-    draw_row = start + n;
-    d.kind = 2;
-  } else {
+    o.row = start + n;
+    o.kind = 2;
+  }
+  return o;
+}
+
+template <bool BF16>
+__device__ __forceinline__ DrawRow draw_row(const SampleParams& P, int row, int kind) {
+  DrawRow d;
+  d.z = P.z + (int64_t)row * P.ld_bytes;
+  d.y = P.y + (int64_t)row * P.ld_bytes;
+  d.c = P.c;
+  const float* st = P.stats + 4 * (int64_t)row;
+  d.cz = st[0];
+  d.lz = st[1];
+  d.cy = st[2];
+  d.ly = st[3];
+  d.kind = kind;
+  return d;
+}
+
+// Tiles [t0, t1) of slice s of a row with n_tiles tiles.
+__device__ __forceinline__ void slice_tiles(int s, int n_tiles, int& t0, int& t1) {
+  const int per = (n_tiles + kSampleSlices - 1) / kSampleSlices;
+  t0 = min(s * per, n_tiles);
+  t1 = min(t0 + per, n_tiles);
+}
+
+// Sums of the tiles of one slice into tsum[0 .. t1-t0) (all four waves), then their sequential sum.
+template <bool BF16>
+__device__ float slice_total(const DrawRow& d, int t0, int t1, int nvec, int vocab, float* tsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = t0 + wave; t < t1; t += kWaves) {
+    const float v = tile_total<BF16>(d, t, nvec, vocab, lane);
+    if (lane == 0) tsum[t - t0] = v;
+  }
+  __syncthreads();
+  float acc = 0.f;
+  for (int t = t0; t < t1; ++t) acc += tsum[t - t0];  // every thread: the same sequence
+  return acc;
+}
+
+// Grid (blocks of this batch, kSampleSlices): the weight sum of one slice of each block's draw row.
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) k_sample_slices(SampleParams P) {
+  __shared__ int s_first;
+  __shared__ float tsum[kMaxSampleTiles / kSampleSlices];
+  const int b = P.block0 + blockIdx.x;
+  const int s = blockIdx.y;
+  const Outcome o = decide<BF16>(P, b, false, &s_first);
+  if (o.kind == 0) return;
+  const DrawRow d = draw_row<BF16>(P, o.row, o.kind);
+  const int n_tiles = (P.nvec + 63) / 64;
+  int t0, t1;
+  slice_tiles(s, n_tiles, t0, t1);
+  const float total = slice_total<BF16>(d, t0, t1, P.nvec, P.vocab, tsum);
+  if (threadIdx.x == 0) P.slices[(int64_t)blockIdx.x * kSampleSlices + s] = total;
+}
+
+// Grid (blocks of this batch): accept length, then the draw: slice, tile, element.
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) k_sample_pick(SampleParams P) {
+  using D = Dec<BF16>;
+  constexpr int EPV = D::EPV;
+  __shared__ int s_first;
+  __shared__ float tsum[kMaxSampleTiles / kSampleSlices];
+  __shared__ float ssum[kSampleSlices];
+  __shared__ int s_tile;
+  __shared__ float s_rem;
+  const int b = P.block0 + blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const Outcome o = decide<BF16>(P, b, true, &s_first);
+  if (tid == 0) P.accept_len[b] = o.bad ? 0 : o.first;
+  if (o.kind == 0) {
     if (tid == 0) P.token[b] = -1;
     return;
   }
-  d.z = P.z + (int64_t)draw_row * P.ld_bytes;
-  d.y = P.y + (int64_t)draw_row * P.ld_bytes;
-  d.c = P.c;
-  {
-    const float* st = P.stats + 4 * (int64_t)draw_row;
-    d.cz = st[0];
-    d.lz = st[1];
-    d.cy = st[2];
-    d.ly = st[3];
-  }
-  const int nvec = P.nvec;
-  const int n_tiles = (nvec + 63) / 64;
-
-  // ---- pass 1: per tile (64 vectors, one wave) the sum of its weights, from the same wave scan
-  // that pass 2 repeats inside the chosen tile; a residual that vanishes everywhere falls back to q
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    for (int t = wave; t < n_tiles; t += kWaves) {
-      float w[EPV];
-      vector_weights<BF16>(d, t * 64 + lane, nvec, P.vocab, w);
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) s += w[e];
-      s = wave_scan(s, lane);
-      if (lane == 63) tile_sum[t] = s;
+  const int n_tiles = (P.nvec + 63) / 64;
+  DrawRow d = draw_row<BF16>(P, o.row, o.kind);
+  if (tid < kSampleSlices) ssum[tid] = P.slices[(int64_t)blockIdx.x * kSampleSlices + tid];
+  __syncthreads();
+  float total = 0.f;
+  for (int s = 0; s < kSampleSlices; ++s) total += ssum[s];
+  if (d.kind == 1 && !(total > 0.f)) {
+    // the residual vanished everywhere: draw from q, whose slice sums this workgroup forms itself
+    // (rare: q <= p at every index in fp32)
+    d.kind = 2;
+    for (int s = 0; s < kSampleSlices; ++s) {
+      int t0, t1;
+      slice_tiles(s, n_tiles, t0, t1);
+      const float v = slice_total<BF16>(d, t0, t1, P.nvec, P.vocab, tsum);
+      __syncthreads();  // tsum is reused by the next slice
+      if (tid == 0) ssum[s] = v;
     }
     __syncthreads();
-    if (d.kind == 2) break;
-    // any positive tile?
-    int any = 0;
-    for (int t = tid; t < n_tiles; t += kThreads) any |= tile_sum[t] > 0.f;
-    if (__syncthreads_or(any)) break;
-    d.kind = 2;
+    total = 0.f;
+    for (int s = 0; s < kSampleSlices; ++s) total += ssum[s];
   }
-
-  // ---- find the tile: lane l of wave 0 owns a contiguous group of tiles
-  if (wave == 0) {
-    const int g = (n_tiles + 63) / 64;
-    const int t0 = min(lane * g, n_tiles), t1 = min(t0 + g, n_tiles);
-    float own = 0.f;
-    for (int t = t0; t < t1; ++t) own += tile_sum[t];
-    const float incl = wave_scan(own, lane);
-    const float total = __shfl(incl, 63);
-    const float target = P.u_resample[b] * total;
-    const float before = __shfl_up(incl, 1);
-    const float lo = lane == 0 ? 0.f : before;
-    const bool here = lo <= target && target < incl;
-    const uint64_t m = __ballot(here);
-    if (m) {
-      const int l = __ffsll((unsigned long long)m) - 1;
-      if (lane == l) {
-        float acc = lo;
-        int tile = -1;
-        float rem = 0.f;
-        int last_pos = -1;
-        for (int t = t0; t < t1; ++t) {
-          if (tile_sum[t] > 0.f) last_pos = t;
-          if (acc + tile_sum[t] > target) {
-            tile = t;
-            rem = target - acc;
-            break;
-          }
-          acc += tile_sum[t];
-        }
-        if (tile < 0) {  // rounding left the target at the group's end
-          tile = last_pos;
-          rem = tile_sum[last_pos];
-        }
-        s_tile = tile;
-        s_rem = rem;
+  const float target = P.u_resample[b] * total;
+  // the slice: first whose running sum passes the target; at a rounding edge the last with weight
+  int sl = -1;
+  float rem = 0.f;
+  {
+    float acc = 0.f;
+    int last = -1;
+    for (int s = 0; s < kSampleSlices; ++s) {
+      if (ssum[s] > 0.f) last = s;
+      if (sl < 0 && acc + ssum[s] > target) {
+        sl = s;
+        rem = target - acc;
       }
-    } else if (lane == 0) {  // u * total rounded up to total: the last tile with weight
-      int tile = -1;
-      for (int t = n_tiles - 1; t >= 0; --t)
-        if (tile_sum[t] > 0.f) {
-          tile = t;
-          break;
-        }
-      s_tile = tile;
-      s_rem = tile >= 0 ? tile_sum[tile] : 0.f;
+      if (sl < 0) acc += ssum[s];
+    }
+    if (sl < 0) {
+      sl = last;
+      rem = last >= 0 ? ssum[last] : 0.f;
     }
   }
+  if (sl < 0) {  // no weight at all
+    if (tid == 0) P.token[b] = -1;
+    return;
+  }
+  // the tile inside the slice, from the same tile sums the slice total was made of
+  int t0, t1;
+  slice_tiles(sl, n_tiles, t0, t1);
+  slice_total<BF16>(d, t0, t1, P.nvec, P.vocab, tsum);
+  if (tid == 0) {
+    float acc = 0.f;
+    int tile = -1, last = -1;
+    float r2 = 0.f;
+    for (int t = t0; t < t1; ++t) {
+      const float v = tsum[t - t0];
+      if (v > 0.f) last = t;
+      if (acc + v > rem) {
+        tile = t;
+        r2 = rem - acc;
+        break;
+      }
+      acc += v;
+    }
+    if (tile < 0) {
+      tile = last;
+      r2 = last >= 0 ? tsum[last - t0] : 0.f;
+    }
+    s_tile = tile;
+    s_rem = r2;
+  }
   __syncthreads();
-
-  // ---- pass 2: inside the tile, the same wave scan over its 64 vectors, then one lane's elements
+  // the element inside the tile: the same wave scan over its 64 vectors, then one lane's elements
   if (wave == 0) {
     const int tile = s_tile;
     int idx = -1;
     if (tile >= 0) {
-      const float rem = s_rem;
+      const float r = s_rem;
       const int v = tile * 64 + lane;
       float w[EPV];
-      vector_weights<BF16>(d, v, nvec, P.vocab, w);
-      float s = 0.f;
+      vector_weights<BF16>(d, v, P.nvec, P.vocab, w);
+      float sv = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) s += w[e];
-      const float incl = wave_scan(s, lane);
+      for (int e = 0; e < EPV; ++e) sv += w[e];
+      const float incl = wave_scan(sv, lane);
       const float before = __shfl_up(incl, 1);
       const float lo = lane == 0 ? 0.f : before;
-      // last positive weight of this lane's vector (for the edge cases)
-      int lastp = -1;
+      int lastp = -1;  // last positive weight of this lane's vector (for the edge cases)
 #pragma unroll
       for (int e = 0; e < EPV; ++e) lastp = w[e] > 0.f ? v * EPV + e : lastp;
-      const bool here = lo <= rem && rem < incl;
-      const uint64_t m = __ballot(here);
-      int pick = -1;
+      const uint64_t m = __ballot(lo <= r && r < incl);
       if (m) {
         const int l = __ffsll((unsigned long long)m) - 1;
+        int pick = -1;
         if (lane == l) {
           float acc = lo;
 #pragma unroll
           for (int e = 0; e < EPV; ++e) {
             acc += w[e];
-            if (pick < 0 && acc > rem) pick = v * EPV + e;
+            if (pick < 0 && acc > r) pick = v * EPV + e;
           }
           if (pick < 0) pick = lastp;
         }
-        pick = __shfl(pick, l);
-      } else {  // rem at or past the tile's end: the tile's last positive weight
+        idx = __shfl(pick, l);
+      } else {  // r at or past the tile's end: the tile's last positive weight
         int best = lastp;
 #pragma unroll
         for (int k = 32; k >= 1; k >>= 1) best = max(best, __shfl_xor(best, k));
-        pick = best;
+        idx = best;
       }
-      idx = pick;
     }
     if (lane == 0) P.token[b] = idx;
   }
@@ -426,16 +492,22 @@ __global__ void __launch_bounds__(kThreads) k_sample_verify(SampleParams P) {
 }  // namespace
 
 hipError_t launch_sample_verify(const SampleParams& p, int in_bf16, hipStream_t s) {
-  SampleParams copy = p;
-  void* args[] = {&copy};
+  SampleParams q = p;
+  void* args[] = {&q};
   if (p.n_rows > 0) {
     void* fn = in_bf16 ? (void*)k_row_lse_t<true> : (void*)k_row_lse_t<false>;
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.n_rows), dim3(kThreads), args, 0, s);
     if (e != hipSuccess) return e;
   }
-  if (p.n_blocks > 0) {
-    void* fn = in_bf16 ? (void*)k_sample_verify<true> : (void*)k_sample_verify<false>;
-    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.n_blocks), dim3(kThreads), args, 0, s);
+  // blocks in batches whose slice sums fit the workspace
+  for (int32_t b0 = 0; b0 < p.n_blocks; b0 += kSampleBatch) {
+    q.block0 = b0;
+    const unsigned nb = (unsigned)min(p.n_blocks - b0, kSampleBatch);
+    void* f1 = in_bf16 ? (void*)k_sample_slices<true> : (void*)k_sample_slices<false>;
+    hipError_t e = hipLaunchKernel(f1, dim3(nb, kSampleSlices), dim3(kThreads), args, 0, s);
+    if (e != hipSuccess) return e;
+    void* f2 = in_bf16 ? (void*)k_sample_pick<true> : (void*)k_sample_pick<false>;
+    e = hipLaunchKernel(f2, dim3(nb), dim3(kThreads), args, 0, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

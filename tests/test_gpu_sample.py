@@ -190,6 +190,17 @@ def test_sample_edge_cases_and_flags(lib):
     assert np.array_equal(got["accept_len"], np.minimum(Lfull, np.diff(off)))
     _check_all(zx, yx, off, Lfull, draft2, np.zeros(n), ur, 1.3, got)
 
+    # z = y with a rejected (out-of-range) proposal: the residual q - p is zero everywhere, so the
+    # draw falls back to q at that row
+    draft3 = draft2.copy()
+    draft3[0] = -5
+    got = _run(lib, yt, yt, off, Lfull, draft3, ua, ur, 1.0)
+    assert lib.read_flags(clear=True) == lib.OPD_FLAG_BAD_TOKEN
+    ref = S.verify_sample(yx, yx, off, Lfull, draft3, ua, ur, 1.0)
+    assert ref["trace"][0]["draw"] == (0, "target")
+    assert got["accept_len"][0] == 0
+    _check_all(yx, yx, off, Lfull, draft3, ua, ur, 1.0, got)
+
 
 def test_sample_small_temperature_matches_greedy(lib):
     """At T = 0.02 on rows whose maxima lead by >= 0.5 the rule reduces to greedy verification."""
