@@ -1,8 +1,7 @@
 // Stochastic verification at a sampling temperature (speculative sampling) of packed draft blocks.
 //
 // The pages name temperature as a parameter to tune when the drafter is combined with the target
-// ("AdaFlash: Adaptive Speculative Decoding via On-Policy Distilled Diffusion Drafters", skills
-// directory page, section "Implementation Steps") but give no acceptance rule for it; the rule here
+// ("Adaflash Adaptive Speculative Decoding", skills-directory card, section "Implementation Steps") but give no acceptance rule for it; the rule here
 // is the published speculative-sampling one (Leviathan et al. 2023; Chen et al. 2023): a proposal x
 // at row r is kept when u_r p_r(x) <= q_r(x), with p = softmax(z / T), q = softmax(y / T); at the
 // first rejection the output token is drawn from max(0, q - p) (normalised), after a fully accepted

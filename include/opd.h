@@ -166,9 +166,8 @@ opd_status_t opd_length_head_loss(const int32_t* target_top1, const int32_t* dra
 
 /*
  * Stochastic verification at a sampling temperature (speculative sampling). The pages name the
- * temperature as a parameter to tune when drafter and target are combined ("AdaFlash: Adaptive
- * Speculative Decoding via On-Policy Distilled Diffusion Drafters", skills directory page, section
- * "Implementation Steps") but give no rule for it; the rule is the published speculative-sampling
+ * temperature as a parameter to tune when drafter and target are combined ("Adaflash Adaptive
+ * Speculative Decoding", skills-directory card, section "Implementation Steps") but give no rule for it; the rule is the published speculative-sampling
  * one (Leviathan et al. 2023; Chen et al. 2023). With p_r = softmax(z_r / T), q_r = softmax(y_r / T)
  * and x_r = draft_tokens[r], per packed block b (rows s = offsets[b] .. offsets[b+1]-1, n_b rows,
  * n = clamp(L[b], 0, n_b)):

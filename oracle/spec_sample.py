@@ -6,8 +6,8 @@ may import it; it shares no code with the product library.
 
 Sources, by page title and section:
 
-* "AdaFlash: Adaptive Speculative Decoding via On-Policy Distilled Diffusion Drafters" (skills
-  directory page), section "Implementation Steps": temperature is one of the parameters to tune
+* "Adaflash Adaptive Speculative Decoding" (skills-directory card), section "Implementation
+  Steps": temperature is one of the parameters to tune
   when the drafter is combined with the target for speculative decoding.
 * "AdaFlash: Adaptive Speculative Decoding with Online Self-Improvement for High-Concurrency LLM
   Inference" (besthub.dev article), section "2. Adaptive Length Head for Token-Level Variance": the
