@@ -1,11 +1,12 @@
 // Stochastic verification at a sampling temperature (speculative sampling) of packed draft blocks.
 //
 // The pages name temperature as a parameter to tune when the drafter is combined with the target
-// ("Adaflash Adaptive Speculative Decoding", skills-directory card, section "Implementation Steps") but give no acceptance rule for it; the rule here
-// is the published speculative-sampling one (Leviathan et al. 2023; Chen et al. 2023): a proposal x
-// at row r is kept when u_r p_r(x) <= q_r(x), with p = softmax(z / T), q = softmax(y / T); at the
-// first rejection the output token is drawn from max(0, q - p) (normalised), after a fully accepted
-// budget n < n_b from q of the next row. Blocks are the packed layout of "AdaFlash: Adaptive
+// ("Adaflash Adaptive Speculative Decoding", skills-directory card, section "Implementation
+// Steps") but give no acceptance rule for it; the rule here is the published speculative-sampling
+// one (Leviathan et al. 2023; Chen et al. 2023): a proposal x at row r is kept when
+// u_r p_r(x) <= q_r(x), with p = softmax(z / T), q = softmax(y / T); at the first rejection the
+// output token is drawn from max(0, q - p) (normalised), after a fully accepted budget n < n_b from
+// q of the next row. Blocks are the packed layout of "AdaFlash: Adaptive
 // Speculative Decoding with Online Self-Improvement ..." (besthub.dev article), sections "2. Adaptive
 // Length Head for Token-Level Variance" and "Infrastructure: Async Training & Variable-Length
 // Batching".

@@ -167,9 +167,10 @@ opd_status_t opd_length_head_loss(const int32_t* target_top1, const int32_t* dra
 /*
  * Stochastic verification at a sampling temperature (speculative sampling). The pages name the
  * temperature as a parameter to tune when drafter and target are combined ("Adaflash Adaptive
- * Speculative Decoding", skills-directory card, section "Implementation Steps") but give no rule for it; the rule is the published speculative-sampling
- * one (Leviathan et al. 2023; Chen et al. 2023). With p_r = softmax(z_r / T), q_r = softmax(y_r / T)
- * and x_r = draft_tokens[r], per packed block b (rows s = offsets[b] .. offsets[b+1]-1, n_b rows,
+ * Speculative Decoding", skills-directory card, section "Implementation Steps") but give no rule
+ * for it; the rule is the published speculative-sampling one (Leviathan et al. 2023; Chen et al.
+ * 2023). With p_r = softmax(z_r / T), q_r = softmax(y_r / T) and x_r = draft_tokens[r], per
+ * packed block b (rows s = offsets[b] .. offsets[b+1]-1, n_b rows,
  * n = clamp(L[b], 0, n_b)):
  *   - rows s .. s+n-1 are verified in order; row r's proposal is accepted when
  *     u_accept[r] * p_r(x_r) <= q_r(x_r); accept_len[b] = rows accepted before the first rejection;
