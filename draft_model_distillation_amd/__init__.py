@@ -3,7 +3,8 @@
 The computation lives in hand-written gfx950 HIP kernels behind the C ABI of include/opd.h
 (libopd_mi355x.so, built by ``draft_model_distillation_amd.build``). This package only binds it:
 
-    opd_loss_fwd, opd_loss_bwd, verify_accept_len, opd_fused_fwd_bwd_verify, verify_sample
+    opd_loss_fwd, opd_loss_bwd, verify_accept_len, opd_fused_fwd_bwd_verify, verify_sample,
+    lmhead_fused_fwd_bwd_verify
 
 take torch device tensors and enqueue on torch's current stream.
 """
@@ -19,6 +20,7 @@ from ._binding import (  # noqa: F401
     OPD_FLAG_SPIN_TIMEOUT,
     OpdError,
     length_head_loss,
+    lmhead_fused_fwd_bwd_verify,
     library_path,
     load_library,
     opd_fused_fwd_bwd_verify,

@@ -30,6 +30,8 @@ EXPORTED_SYMBOLS = (
     "opd_read_flags",
     "opd_length_head_loss",
     "opd_verify_sample",
+    "opd_lmhead_scratch_size",
+    "opd_lmhead_fused_fwd_bwd_verify",
     "opd_capacity_init",
     "opd_capacity_observe",
     "opd_pack_first_fit",
@@ -95,6 +97,12 @@ def load_library(require_torch_runtime: bool = True) -> ctypes.CDLL:
         lib.opd_verify_sample.restype = i32
         lib.opd_verify_sample.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(OpdBlocks), vp, vp, vp,
                                           ctypes.c_float, vp, vp, vp, vp, sz, vp]
+        lib.opd_lmhead_scratch_size.restype = sz
+        lib.opd_lmhead_scratch_size.argtypes = [i64, i64, i64]
+        lib.opd_lmhead_fused_fwd_bwd_verify.restype = i32
+        lib.opd_lmhead_fused_fwd_bwd_verify.argtypes = [vp, vp, i64, vp, i32, i64, i64, i64, ctypes.POINTER(OpdBlocks),
+                                                        ctypes.c_float, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                        vp, sz, i64, vp, sz, vp]
         lib.opd_stream_probe.restype = i32
         lib.opd_stream_probe.argtypes = [vp, vp, vp, sz, vp]
         lib.opd_set_spin_limit.restype = None
@@ -384,6 +392,53 @@ def verify_sample(z, y, offsets, lengths, draft_tokens, u_accept, u_resample, te
                                _ptr(o["token"]) if blocks.n_blocks else None, o["row_lse"].data_ptr(),
                                ws.data_ptr(), ws.numel(), _stream(dev))
     _check("opd_verify_sample", st)
+    return o
+
+
+def lmhead_fused_fwd_bwd_verify(h, W, y, offsets, lengths, alpha: float, tau: float, grad_loss=None,
+                                chunk_rows: int = 2048, want_dh: bool = True, want_dW: bool = True, scratch=None,
+                                ws=None, out=None):
+    """OPD loss fused with the vocabulary projection z = h W^T (opd_lmhead_fused_fwd_bwd_verify).
+
+    h [R, H] bf16, W [V, H] bf16, y [R, V] fp32 (rows may be padded to a 16-byte pitch). Returns a dict
+    with loss, target_top1, draft_top1, row_stats, accept_len (if blocks), dh [R, H] f32 and dW [V, H]
+    f32. ``out`` may hold preallocated tensors under the same keys and ``scratch`` a uint8 device
+    tensor of at least opd_lmhead_scratch_size bytes, so that repeated calls allocate nothing.
+    """
+    torch = _torch()
+    lib = load_library()
+    yp, rows, vocab, ld = _matrix(y, "y")
+    for name, t in (("h", h), ("W", W)):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 2-D bfloat16 tensor")
+    hidden = W.shape[1]
+    if W.shape[0] != vocab or h.shape != (rows, hidden):
+        raise ValueError("shapes must be h [R, H], W [V, H], y [R, V]")
+    dev = y.device
+    ws = workspace(dev) if ws is None else ws
+    blocks = _blocks(offsets, lengths)
+    n_blocks = blocks.n_blocks if blocks is not None else 0
+    rc = max(1, min(int(chunk_rows), max(rows, 1)))
+    need = lib.opd_lmhead_scratch_size(rc, vocab, ld)
+    if scratch is None or scratch.numel() < need:
+        scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    o = dict(out) if out is not None else {}
+    if "loss" not in o:
+        o["loss"] = torch.empty(rows, dtype=torch.float32, device=dev)
+        o["target_top1"] = torch.empty(rows, dtype=torch.int32, device=dev)
+        o["draft_top1"] = torch.empty(rows, dtype=torch.int32, device=dev)
+        o["row_stats"] = torch.empty(rows, 8, dtype=torch.float32, device=dev)
+        o["accept_len"] = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+        o["dh"] = torch.empty(rows, hidden, dtype=torch.float32, device=dev) if want_dh else None
+        o["dW"] = torch.empty(vocab, hidden, dtype=torch.float32, device=dev) if want_dW else None
+    st = lib.opd_lmhead_fused_fwd_bwd_verify(
+        h.data_ptr(), W.data_ptr(), hidden, yp, _dtype_code(y), rows, vocab, ld,
+        ctypes.byref(blocks) if blocks is not None else None, float(alpha), float(tau), _ptr(grad_loss),
+        o["loss"].data_ptr(), o["target_top1"].data_ptr(), o["draft_top1"].data_ptr(), o["row_stats"].data_ptr(),
+        _ptr(o["dh"]), _ptr(o["dW"]), _ptr(o["accept_len"]) if n_blocks else None, scratch.data_ptr(),
+        scratch.numel(), rc, ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("opd_lmhead_fused_fwd_bwd_verify", st)
+    o["scratch"] = scratch
     return o
 
 

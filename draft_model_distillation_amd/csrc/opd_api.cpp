@@ -412,6 +412,80 @@ opd_status_t opd_verify_sample(const void* z, const void* y, opd_dtype_t dt, int
   return OPD_OK;
 }
 
+static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+size_t opd_lmhead_scratch_size(int64_t chunk_rows, int64_t vocab, int64_t ld_y) {
+  if (chunk_rows <= 0 || vocab <= 0 || ld_y < vocab) return 0;
+  // logits chunk: fp32 with the pitch of y (the row kernel reads both with one pitch); dz chunk: bf16
+  const int64_t zb = round_up(chunk_rows * ld_y * 4, 256);
+  const int64_t db = round_up(chunk_rows * round_up(vocab, 8) * 2, 256);
+  return (size_t)(zb + db);
+}
+
+opd_status_t opd_lmhead_fused_fwd_bwd_verify(const void* h, const void* W, int64_t hidden, const void* y,
+                                             opd_dtype_t dt_y, int64_t n_rows, int64_t vocab, int64_t ld_y,
+                                             const opd_blocks_t* blocks, float alpha, float tau,
+                                             const float* grad_loss, float* loss, int32_t* target_top1,
+                                             int32_t* draft_top1, float* row_stats, float* dh, float* dW,
+                                             int32_t* accept_len, void* scratch, size_t scratch_bytes,
+                                             int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
+  opd_status_t s = check_logits(y, y, dt_y, n_rows, vocab, ld_y);
+  if (s != OPD_OK) return s;
+  if (dt_y != OPD_F32) return fail(OPD_ERR_DTYPE, "y must be fp32 (the logits chunk it is paired with is fp32)");
+  if (hidden <= 0 || hidden > INT32_MAX) return fail(OPD_ERR_SHAPE, "hidden must be in [1, 2^31)");
+  if (hidden % 8) return fail(OPD_ERR_ALIGN, "hidden must be a multiple of 8 (16-byte bf16 rows)");
+  if (vocab > 0 && (!W || (n_rows > 0 && !h))) return fail(OPD_ERR_NULL, "h and W must be non-NULL");
+  if (n_rows > 0 && (!loss || !target_top1 || !row_stats))
+    return fail(OPD_ERR_NULL, "loss, target_top1 and row_stats must be non-NULL");
+  if (!aligned16(h) || !aligned16(W) || !aligned16(dh) || !aligned16(dW))
+    return fail(OPD_ERR_ALIGN, "h, W, dh and dW must be 16-byte aligned");
+  if ((s = check_blocks(blocks, false)) != OPD_OK) return s;
+  if (blocks && blocks->n_blocks > 0 && !accept_len) return fail(OPD_ERR_NULL, "accept_len must be non-NULL");
+  if ((s = check_params(alpha, tau)) != OPD_OK) return s;
+  if ((s = check_ws(ws, ws_bytes)) != OPD_OK) return s;
+  if (chunk_rows <= 0) return fail(OPD_ERR_SHAPE, "chunk_rows must be >= 1");
+  if (n_rows > 0 && !draft_top1 && blocks && blocks->n_blocks > 0)
+    return fail(OPD_ERR_NULL, "draft_top1 is needed for verification");
+  const int64_t rc_max = chunk_rows < n_rows ? chunk_rows : n_rows;
+  if (n_rows == 0) {
+    if (dW && vocab > 0) {  // no rows: the gradient of the projection is zero
+      hipError_t e = opd::launch_fill_u32(reinterpret_cast<uint32_t*>(dW), 0u, (size_t)vocab * hidden, stream);
+      if (e != hipSuccess) return hip_fail(e, "clearing dW");
+    }
+    return run_accept(blocks, 0, draft_top1, target_top1, accept_len, ws, stream);
+  }
+  if (!scratch || scratch_bytes < opd_lmhead_scratch_size(rc_max, vocab, ld_y))
+    return fail(OPD_ERR_WORKSPACE, "scratch missing or smaller than opd_lmhead_scratch_size()");
+  if (!aligned16(scratch)) return fail(OPD_ERR_ALIGN, "scratch must be 16-byte aligned");
+  const int64_t ld_dz = round_up(vocab, 8);
+  float* zc = static_cast<float*>(scratch);
+  uint16_t* dzc = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(scratch) + round_up(rc_max * ld_y * 4, 256));
+  const uint8_t* hb = static_cast<const uint8_t*>(h);
+  const uint8_t* yb = static_cast<const uint8_t*>(y);
+  // Row-major matrices seen column-major: h^T [hidden x rows], W^T [hidden x vocab], z^T [vocab x rows].
+  for (int64_t r0 = 0; r0 < n_rows; r0 += chunk_rows) {
+    const int64_t rc = (n_rows - r0) < chunk_rows ? (n_rows - r0) : chunk_rows;
+    const void* hc = hb + r0 * hidden * 2;
+    // z^T = W h^T  (vocab x rc)
+    if ((s = opd::gemm_bf16_f32(true, false, vocab, rc, hidden, W, hidden, hc, hidden, 0.f, zc, ld_y, stream)) != OPD_OK)
+      return s;
+    if ((s = run_team(opd::kFused, zc, yb + r0 * ld_y * 4, OPD_F32, rc, vocab, ld_y, alpha, tau,
+                      grad_loss ? grad_loss + r0 : nullptr, loss + r0, target_top1 + r0,
+                      draft_top1 ? draft_top1 + r0 : nullptr, row_stats + 8 * r0, dzc, OPD_BF16, ld_dz, ws,
+                      stream)) != OPD_OK)
+      return s;
+    // dh^T = W^T dz^T  (hidden x rc)
+    if (dh && (s = opd::gemm_bf16_f32(false, false, hidden, rc, vocab, W, hidden, dzc, ld_dz, 0.f, dh + r0 * hidden,
+                                      hidden, stream)) != OPD_OK)
+      return s;
+    // dW^T (+)= h^T dz  (hidden x vocab), accumulated over the chunks
+    if (dW && (s = opd::gemm_bf16_f32(false, true, hidden, vocab, rc, hc, hidden, dzc, ld_dz, r0 == 0 ? 0.f : 1.f, dW,
+                                      hidden, stream)) != OPD_OK)
+      return s;
+  }
+  return run_accept(blocks, n_rows, draft_top1, target_top1, accept_len, ws, stream);
+}
+
 opd_status_t opd_read_flags(void* ws, size_t ws_bytes, int clear, uint32_t* flags, hipStream_t stream) {
   if (!flags) return fail(OPD_ERR_NULL, "flags must be non-NULL");
   opd_status_t s = check_ws(ws, ws_bytes);

@@ -137,6 +137,11 @@ hipError_t launch_stream_probe(const void* a, const void* b, void* c, size_t n_v
 hipError_t launch_length_head(const LengthHeadParams& p, hipStream_t s);  // opd_epilogue.hip
 hipError_t launch_sample_verify(const SampleParams& p, int in_bf16, hipStream_t s);  // opd_sample.hip
 
+// Column-major C[m x n] = op(A) op(B) + beta C with bf16 A, B and fp32 C, through rocBLAS
+// (opd_lmhead.cpp). op = transpose when trans_* is set.
+opd_status_t gemm_bf16_f32(bool trans_a, bool trans_b, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
+                           const void* B, int64_t ldb, float beta, float* C, int64_t ldc, hipStream_t stream);
+
 // Records the detail text returned by opd_last_error() on this thread (opd_api.cpp).
 opd_status_t record_error(opd_status_t s, const char* msg);
 

@@ -202,6 +202,41 @@ opd_status_t opd_verify_sample(const void* z, const void* y, opd_dtype_t dt, int
                                size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The OPD loss fused with the drafter's vocabulary projection: the logits z = h W^T are never held
+ * for the whole batch. The loss is the one above ("AdaFlash: Adaptive Speculative Decoding with
+ * Online Self-Improvement ...", section "1. On-Policy Distillation (OPD) for Domain Adaptation":
+ * the drafter is what the online update trains); the pages show neither the drafter's head nor its
+ * sizes, so h is read as the drafter's final hidden states and W as its projection (no bias), and
+ * the gradient flows to both. Rows are processed in chunks of chunk_rows: per chunk, z (fp32) =
+ * h W^T into scratch (rocBLAS, bf16 operands, fp32 accumulation), the fused loss / gradient / top-1
+ * pass of opd_fused_fwd_bwd_verify over that chunk (dz as bf16 into scratch), dh = dz W and
+ * dW (+)= dz^T h (rocBLAS); then the accept lengths of all blocks.
+ *   h          [n_rows, hidden] bf16, row-major, pitch hidden (hidden a multiple of 8).
+ *   W          [vocab, hidden] bf16, row-major, pitch hidden.
+ *   y          [n_rows, ld_y] target logits, dt_y must be OPD_F32 (the logits chunk is fp32 and the
+ *              row kernel reads both with one pitch); ld_y >= vocab, pitch a multiple of 16 bytes.
+ *   loss, target_top1, draft_top1, row_stats, accept_len: as opd_fused_fwd_bwd_verify (draft_top1
+ *              may be NULL only without blocks); grad_loss [n_rows] or NULL.
+ *   dh         [n_rows, hidden] f32 out (overwritten), or NULL to skip.
+ *   dW         [vocab, hidden] f32 out (overwritten: the sum over all chunks), or NULL to skip.
+ *   scratch    caller device memory of at least opd_lmhead_scratch_size(min(chunk_rows, n_rows),
+ *              vocab, ld_y) bytes, 16-byte aligned: one chunk of fp32 logits and of bf16 dz.
+ * dh and dW are formed from the bf16-rounded dz of the row kernel. The three products go through
+ * rocBLAS, which keeps one handle (and its own device workspace) per device for the process; the
+ * handle has atomics disabled, so results are deterministic.
+ * Errors: OPD_ERR_NULL, OPD_ERR_SHAPE, OPD_ERR_DTYPE (dt_y not OPD_F32), OPD_ERR_ALIGN,
+ * OPD_ERR_PARAM, OPD_ERR_WORKSPACE (ws or scratch too small), OPD_ERR_HIP (including rocBLAS errors).
+ */
+size_t opd_lmhead_scratch_size(int64_t chunk_rows, int64_t vocab, int64_t ld_y);
+opd_status_t opd_lmhead_fused_fwd_bwd_verify(const void* h, const void* W, int64_t hidden, const void* y,
+                                             opd_dtype_t dt_y, int64_t n_rows, int64_t vocab, int64_t ld_y,
+                                             const opd_blocks_t* blocks, float alpha, float tau,
+                                             const float* grad_loss, float* loss, int32_t* target_top1,
+                                             int32_t* draft_top1, float* row_stats, float* dh, float* dW,
+                                             int32_t* accept_len, void* scratch, size_t scratch_bytes,
+                                             int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Host-side batch scheduling ("AdaFlash: Adaptive Speculative Decoding with Online Self-Improvement
  * for High-Concurrency LLM Inference", section "Infrastructure: Async Training & Variable-Length
  * Batching": requests with different predicted verification lengths are packed into compact batches

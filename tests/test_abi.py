@@ -125,6 +125,33 @@ def test_verify_sample_validation(lib):
                                  None, None, None, 1.0, None, None, None, WS, ws, None) == 0
 
 
+def test_lmhead_validation(lib):
+    ws = lib.opd_workspace_size()
+    sc = lib.opd_lmhead_scratch_size(16, 64, 64)
+    assert sc >= 16 * 64 * 4 + 16 * 64 * 2
+    assert lib.opd_lmhead_scratch_size(0, 64, 64) == 0
+
+    def call(h=P, W=P, H=32, y=P, dt=F32, n=4, v=64, ld=64, a=0.5, t=0.05, loss=P, top=P, dtop=P, st=P, dh=P,
+             dW=P, scratch=P, scb=sc, rc=16, wsp=WS, wsb=ws, blocks=None):
+        b = ctypes.byref(blocks) if blocks is not None else None
+        return lib.opd_lmhead_fused_fwd_bwd_verify(h, W, H, y, dt, n, v, ld, b, a, t, None, loss, top, dtop, st, dh,
+                                                   dW, None, scratch, scb, rc, wsp, wsb, None)
+
+    # (a call that passes validation would launch kernels on the fake pointers: never made here)
+    assert call(dt=BF16) == 3
+    assert call(y=None) == 1 and call(h=None) == 1 and call(W=None) == 1
+    assert call(loss=None) == 1 and call(st=None) == 1
+    assert call(H=0) == 2 and call(H=12) == 4
+    assert call(h=P + 8) == 4
+    assert call(rc=0) == 2
+    assert call(a=2.0) == 5
+    need = lib.opd_lmhead_scratch_size(4, 64, 64)  # 4 rows: one chunk of min(rc, n) rows
+    assert call(scratch=None) == 6 and call(scb=need - 1) == 6
+    assert call(wsb=8) == 6
+    assert call(blocks=m._binding.OpdBlocks(P, P, 3)) == 1  # accept_len missing
+    assert call(n=0, scratch=None, dW=None) == 0  # no rows, nothing to clear: no HIP call
+
+
 def test_zero_rows_accepts_null_buffers(lib):
     ws = lib.opd_workspace_size()
     # nothing to do: no HIP call is needed and NULL data pointers are fine
