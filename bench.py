@@ -140,6 +140,8 @@ def main():
     ap.add_argument("--workload", default="train", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-blocks", type=int, default=512, help="blocks of the workload timed on the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lmhead", dest="lmhead", action="store_false",
+                    help="skip timing the lm_head-fused path beside the step")
     ap.add_argument("--profile", action="store_true",
                     help="for rocprofv3 counter runs: no CPU baseline, and after the timed steps a plain "
                          "1 GiB device copy (torch copy_) whose FETCH_SIZE / WRITE_SIZE calibrate the counters")
@@ -276,6 +278,36 @@ def main():
             print("[bench] device flags raised by the sampling verification", file=sys.stderr)
             sys.exit(1)
 
+    # lm_head-fused loss (next row): 2048 rows of the workload's target logits (fp32), drafter hidden
+    # states h [2048, 4096] and projection W [V, 4096] (seeded bf16), one chunk of 2048 rows:
+    # logits = h W^T, loss / top-1s / dz, dh = dz W, dW = dz^T h per call
+    lmhead = None
+    if args.lmhead and not args.profile and rec.vocab > 100000 and n >= 2048:
+        R, Hd = 2048, 4096
+        g = torch.Generator(device="cuda").manual_seed(9)
+        hh = torch.randn(R, Hd, generator=g, device=dev).to(torch.bfloat16)
+        Wm = (torch.randn(rec.vocab, Hd, generator=g, device=dev) * 0.047).to(torch.bfloat16)
+        y32 = y[:R].float().contiguous()
+        lo = torch.arange(0, R + 1, 16, dtype=torch.int32, device=dev)
+        ll = torch.full((R // 16,), 16, dtype=torch.int32, device=dev)
+        lout = opd.lmhead_fused_fwd_bwd_verify(hh, Wm, y32, lo, ll, rec.alpha, rec.tau, chunk_rows=R, ws=ws)
+        steps = max(1, min(args.steps, 10))
+        ev0.record(stream)
+        for _ in range(steps):
+            opd.lmhead_fused_fwd_bwd_verify(hh, Wm, y32, lo, ll, rec.alpha, rec.tau, chunk_rows=R, ws=ws, out=lout,
+                                            scratch=lout["scratch"])
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        lm_ms = ev0.elapsed_time(ev1) / steps
+        flops = 3 * 2.0 * R * rec.vocab * Hd
+        lmhead = {"rows": R, "hidden": Hd, "ms": lm_ms, "gemm_flops": flops,
+                  "gemm_tflops": flops / (lm_ms * 1e-3) / 1e12,
+                  "frac_of_bf16_peak": flops / (lm_ms * 1e-3) / 2.5e15}
+        if opd.read_flags(ws, clear=True) != 0:
+            print("[bench] device flags raised by the lm_head-fused path", file=sys.stderr)
+            sys.exit(1)
+        del hh, Wm, y32, lout
+
     # host packer: first fit of the workload's requests (their lengths, in order) under a budget
     # of half the workload's rows, per call through the binding
     lengths_np = np.diff(off.cpu().numpy())
@@ -346,6 +378,9 @@ def main():
         "extras": {"length_head_epilogue_us": head_us, "host_packer_us": pack_us,
                    # opd_verify_sample at T = 1 (both kernels) per call; gbs = z and y read once / time
                    "sampling_verify": sample,
+                   # opd_lmhead_fused_fwd_bwd_verify per call (three bf16 GEMMs through rocBLAS + the
+                   # row kernel); gemm_tflops counts the GEMM flops only, against 2.5 PFLOP/s dense bf16
+                   "lmhead_fused": lmhead,
                    "packer_requests": int(lengths_np.size)},
     }
     print(json.dumps(result), flush=True)
