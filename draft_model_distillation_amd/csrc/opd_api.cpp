@@ -120,7 +120,7 @@ opd_status_t device_info(int mode, int in_bf16, int out_bf16, int kidx, int K, i
 }
 
 struct Geometry {
-  int K, G, chunk_vec, nvec, n_teams, grid, xcd_map;
+  int K, G, chunk_vec, nvec, n_teams, grid;
 };
 
 // Split a row of nvec 16-byte vectors over G workgroups of 256 threads x K slots, and choose how
@@ -145,16 +145,12 @@ opd_status_t plan(int mode, int in_bf16, int out_bf16, int64_t n_rows, int64_t v
   int64_t max_teams = capacity / G;
   if (max_teams < 1) return fail(OPD_ERR_SHAPE, "row too wide for the device");
   int64_t teams = n_rows < max_teams ? n_rows : max_teams;
-  // Teams are spread over the XCDs (consecutive workgroups, round-robin dispatch): measured faster
-  // than keeping a team on one XCD, whose L2 is then shared by all rows that XCD streams.
-  const int xcd = 0;
   g->K = K;
   g->G = G;
   g->chunk_vec = chunk;
   g->nvec = nvec;
   g->n_teams = (int)teams;
   g->grid = (int)(teams * G);
-  g->xcd_map = xcd;
   return OPD_OK;
 }
 
@@ -192,7 +188,6 @@ opd_status_t run_team(int mode, const void* z, const void* y, opd_dtype_t dt, in
   p.G = g.G;
   p.chunk_vec = g.chunk_vec;
   p.n_teams = g.n_teams;
-  p.xcd_map = g.xcd_map;
   p.alpha = alpha;
   p.tau = tau;
   p.grad_loss = grad_loss;

@@ -41,7 +41,6 @@ struct TeamParams {
   int32_t G;          // workgroups per row
   int32_t chunk_vec;  // vectors per chunk (last chunk may be shorter)
   int32_t n_teams;
-  int32_t xcd_map;    // 1: members of a team are dispatched to the same XCD
   float alpha;
   float tau;
   const float* grad_loss;  // nullable

@@ -533,15 +533,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
   const int tid = thread_id();
   const int wave = tid >> 6;
   const int b = block_id_x();
-  int team, chunk;
-  if (P.xcd_map) {
-    const int x = b & 7, local = b >> 3;
-    team = (local / P.G) * 8 + x;
-    chunk = local % P.G;
-  } else {
-    team = b / P.G;
-    chunk = b % P.G;
-  }
+  // consecutive workgroups form a team, so its members land on different XCDs (round-robin
+  // dispatch); keeping a team on one XCD measured slower
+  const int team = b / P.G;
+  const int chunk = b % P.G;
   const int G = P.G;
   const int cv0 = chunk * P.chunk_vec;
   const int clen0 = min(P.chunk_vec, P.nvec - cv0);  // vectors in this chunk (uniform)
