@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -51,11 +52,19 @@ WORKLOAD_TEXT = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed (what the compiler sees)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the code (not the comments) of the row-team kernel's sources."""
     h = hashlib.sha256()
     for f in ("opd_kernels.hip", "opd_internal.h"):
-        with open(os.path.join(ROOT, "draft_model_distillation_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "draft_model_distillation_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -24,10 +24,12 @@
 //            term and use their phase-A sums; the rest (near the peak) are visited element by element
 //   -- exchange 2 --  the two sums
 //   phase C  dz written once (bf16 rounded to nearest even, or fp32)
-// The kernel is VALU-heavy for an HBM stream (about 30 lane-ops and 3.5 exponentials per element),
-// so the per-element work is kept minimal and the per-row work (reductions, exchanges, row
-// constants) runs once per workgroup in wave 0 while the other waves wait at barriers and the SIMDs
-// serve the other resident workgroups. Exchanges use 8-byte [value | flag] units written and
+// The kernel is VALU-heavy for an HBM stream (about 33 VALU instructions per element, 3.5 of them
+// exponentials), so the per-element work is kept minimal and the per-row work (reductions,
+// exchanges, row constants) runs once per workgroup in wave 0 while the other waves wait at
+// barriers and the SIMDs serve the other resident workgroups. A row in an exchange holds up all G
+// members of its team, so from the chunk reductions to the end of each exchange the waves raise
+// their issue priority above the streaming phases of the other workgroups on the CU. Exchanges use 8-byte [value | flag] units written and
 // polled with agent-scope relaxed atomics (sc1: coherent across XCDs without L2 writeback /
 // invalidate); the flag is unique per launch, row iteration and stage, so nothing has to be reset
 // between launches and a stale unit can never be taken for a fresh one. Every wait is bounded and

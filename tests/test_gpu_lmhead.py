@@ -173,3 +173,30 @@ def test_lmhead_benchmark_configuration_sampled_rows(lib):
     torch.cuda.synchronize()
     for k in ("loss", "dh", "dW", "accept_len"):
         assert torch.equal(out[k], out2[k]), k
+
+
+def test_lmhead_optional_outputs_and_empty_batch(lib):
+    """dh / dW may be skipped (their products are not run) and the rest is unchanged; no rows gives
+    a zero dW and no accept lengths to compute."""
+    import torch
+
+    rng, hb, h, Wb, W, y = _problem(6, 20, 520, 32, 0.5)
+    ht, Wt, yt = _dev(lib, hb, Wb, y, 520)
+    off = torch.tensor([0, 8, 20], dtype=torch.int32, device="cuda")
+    L = torch.tensor([8, 12], dtype=torch.int32, device="cuda")
+    full = lib.lmhead_fused_fwd_bwd_verify(ht, Wt, yt, off, L, 0.5, 0.05, chunk_rows=7)
+    part = lib.lmhead_fused_fwd_bwd_verify(ht, Wt, yt, off, L, 0.5, 0.05, chunk_rows=7, want_dh=False, want_dW=False)
+    torch.cuda.synchronize()
+    assert lib.read_flags(clear=True) == 0
+    assert part["dh"] is None and part["dW"] is None
+    for k in ("loss", "target_top1", "draft_top1", "row_stats", "accept_len"):
+        assert torch.equal(full[k], part[k]), k
+    # grad_loss = 0 on every row: zero gradients
+    zero = lib.lmhead_fused_fwd_bwd_verify(ht, Wt, yt, off, L, 0.5, 0.05, chunk_rows=7,
+                                           grad_loss=torch.zeros(20, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(zero["dh"]) == 0 and torch.count_nonzero(zero["dW"]) == 0
+    # no rows
+    e = lib.lmhead_fused_fwd_bwd_verify(ht[:0], Wt, yt[:0], None, None, 0.5, 0.05)
+    torch.cuda.synchronize()
+    assert e["dW"].shape == (520, 32) and torch.count_nonzero(e["dW"]) == 0
