@@ -159,8 +159,8 @@ def main():
         args.no_cpu_baseline = True
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (rows shard across GPUs "
-              "without communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (rows would shard across "
+              "GPUs at block boundaries without communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     t_gen = time.perf_counter()
