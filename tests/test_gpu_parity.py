@@ -261,6 +261,48 @@ def test_vocab_sizes_and_padding(lib, dtype_name, v):
         assert ok, f"row {r}: {msg}"
 
 
+def test_seeded_random_shapes_fused(lib):
+    """A fixed seed draws shapes across the launch plans (one to several workgroups per row, a
+    partial last vector, padded pitches, fp32 / bf16 in and out, random alpha / tau / weights, random
+    blocks) and checks every row of each against the oracle."""
+    import torch
+
+    rng = np.random.default_rng(1234)
+    for case in range(10):
+        dtype_name = ["f32", "bf16"][case % 2]
+        dz_bf16 = bool(rng.integers(0, 2))
+        v = int(rng.choice([5, 300, 2047, 3001, 12289, 40000, 77777]))
+        n = int(rng.integers(1, 40))
+        epv = 8 if dtype_name == "bf16" else 4
+        ld = ((v + epv - 1) // epv) * epv + epv * int(rng.integers(0, 3))
+        z, y = _random_rows(rng, n, v, scale=float(rng.uniform(0.5, 4.0)))
+        zt, zx = _to_dev_padded(z, ld, dtype_name)
+        yt, yx = _to_dev_padded(y, ld, dtype_name)
+        alpha = float(rng.uniform(0, 1))
+        tau = float(rng.choice([0.01, 0.05, 0.2, math.inf]))
+        w = rng.uniform(0.2, 2.0, n).astype(np.float32)
+        cuts = np.sort(rng.choice(np.arange(1, n), size=min(3, n - 1), replace=False)) if n > 1 else np.array([], int)
+        off = np.concatenate([[0], cuts, [n]]).astype(np.int32)
+        L = rng.integers(-1, 18, len(off) - 1).astype(np.int32)
+        _say(f"random case {case}: {dtype_name} V={v} rows={n} ld={ld} dz_bf16={dz_bf16} tau={tau}")
+        out = lib.opd_fused_fwd_bwd_verify(zt, yt, torch.from_numpy(off).cuda(), torch.from_numpy(L).cuda(), alpha,
+                                           tau, grad_loss=torch.from_numpy(w).cuda(),
+                                           dz_dtype=torch.bfloat16 if dz_bf16 else torch.float32)
+        torch.cuda.synchronize()
+        flags = lib.read_flags(clear=True)
+        assert flags == (lib.OPD_FLAG_NEG_L if (L < 0).any() else 0)
+        a_ref, d_ref = O.top1_rows(yx), O.top1_rows(zx)
+        assert np.array_equal(out["target_top1"].cpu().numpy(), a_ref)
+        assert np.array_equal(out["draft_top1"].cpu().numpy(), d_ref)
+        acc_ref, _ = O.accept_lengths(d_ref, a_ref, off, L)
+        assert np.array_equal(out["accept_len"].cpu().numpy(), acc_ref)
+        dz = out["dz"].float().cpu().numpy().astype(np.float64)
+        loss = out["loss"].cpu().numpy()
+        for r in range(n):
+            ok, msg = parity.check_row(zx[r], yx[r], alpha, tau, loss[r], dz[r], bf16_dz=dz_bf16, w=float(w[r]))
+            assert ok, f"case {case} row {r}: {msg}"
+
+
 def test_dz_pad_is_not_written(lib):
     import torch
 
