@@ -280,8 +280,12 @@ def main():
         ev1.record(stream)
         torch.cuda.synchronize()
         sample_ms = ev0.elapsed_time(ev1) / args.steps
-        read_bytes = 2 * n * rec.vocab * (2 if rec.dtype == "bf16" else 4)
-        sample = {"ms": sample_ms, "read_bytes": read_bytes, "gbs": read_bytes / (sample_ms * 1e-3) / 1e9,
+        # algorithmic bytes: z and y of the rows the verification reads (min(L + 1, n_b) per block)
+        nb_h = np.diff(off.cpu().numpy())
+        rows_read = int(np.minimum(np.clip(lens.cpu().numpy(), 0, nb_h) + 1, nb_h).sum())
+        read_bytes = 2 * rows_read * rec.vocab * (2 if rec.dtype == "bf16" else 4)
+        sample = {"ms": sample_ms, "rows_read": rows_read, "read_bytes": read_bytes,
+                  "gbs": read_bytes / (sample_ms * 1e-3) / 1e9,
                   "mean_accept": float(so["accept_len"].float().mean().item())}
         if opd.read_flags(ws, clear=True) != 0:
             print("[bench] device flags raised by the sampling verification", file=sys.stderr)
@@ -385,7 +389,8 @@ def main():
         # over this workload's blocks (includes the binding's output allocation), the host packer
         # per call over this workload's requests, and the speculative-sampling verification
         "extras": {"length_head_epilogue_us": head_us, "host_packer_us": pack_us,
-                   # opd_verify_sample at T = 1 (both kernels) per call; gbs = z and y read once / time
+                   # opd_verify_sample at T = 1 (all kernels) per call; gbs = z and y of the rows the
+                   # verification reads, once, / time
                    "sampling_verify": sample,
                    # opd_lmhead_fused_fwd_bwd_verify per call (three bf16 GEMMs through rocBLAS + the
                    # row kernel); gemm_tflops counts the GEMM flops only, against 2.5 PFLOP/s dense bf16

@@ -363,7 +363,8 @@ def verify_sample(z, y, offsets, lengths, draft_tokens, u_accept, u_resample, te
     """Speculative-sampling verification at a temperature (opd_verify_sample).
 
     Returns a dict: accept_len [B] i32, token [B] i32 (-1 when none), row_lse [R, 4] f32 (reference and
-    log2 of the sum of 2^(x log2(e) / T) for z, then for y). ``out`` may hold preallocated tensors under
+    log2 of the sum of 2^(x log2(e) / T) for z, then for y; written for the rows the verification
+    reads, NaN elsewhere when allocated here). ``out`` may hold preallocated tensors under
     the same keys.
     """
     torch = _torch()
@@ -385,7 +386,7 @@ def verify_sample(z, y, offsets, lengths, draft_tokens, u_accept, u_resample, te
     if "accept_len" not in o:
         o["accept_len"] = torch.empty(blocks.n_blocks, dtype=torch.int32, device=dev)
         o["token"] = torch.empty(blocks.n_blocks, dtype=torch.int32, device=dev)
-        o["row_lse"] = torch.empty(rows, 4, dtype=torch.float32, device=dev)
+        o["row_lse"] = torch.full((rows, 4), float("nan"), dtype=torch.float32, device=dev)
     st = lib.opd_verify_sample(zp, yp, _dtype_code(z), rows, vocab, ld, ctypes.byref(blocks), draft_tokens.data_ptr(),
                                u_accept.data_ptr(), u_resample.data_ptr(), float(temperature),
                                _ptr(o["accept_len"]) if blocks.n_blocks else None,

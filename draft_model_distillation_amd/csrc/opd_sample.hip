@@ -12,7 +12,8 @@
 // Batching".
 //
 // Three kernels:
-//   k_row_lse_t     one workgroup per row: one streaming read of z and y (4V bytes for bf16) giving
+//   k_row_lse_t     one workgroup per row the verification can read (a block's n verified rows and
+//                   the row after them): one streaming read of z and y (4V bytes for bf16) giving
 //                   log2 sum 2^(x log2e / T) of both rows as (reference, log2 of the sum relative to
 //                   it), with per-vector references so that no row maximum is needed first.
 //   k_sample_slices (block, slice) workgroups: each takes the block's accept decisions (one lane per
@@ -38,6 +39,7 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kWaves = kThreads / 64;
+constexpr unsigned kRowSlots = 17;  // a k = 16 block's verified rows and its bonus row
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -106,11 +108,10 @@ __device__ __forceinline__ void combine(float& ref, float& sum, float ref2, floa
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads) k_row_lse_t(SampleParams P) {
+__device__ void row_lse_one(const SampleParams& P, int row) {
   using D = Dec<BF16>;
   constexpr int EPV = D::EPV;
-  constexpr int U = 4;  // vectors per tensor in flight per thread
-  const int row = blockIdx.x;
+  constexpr int U = 8;  // vectors per tensor in flight per thread
   const int tid = threadIdx.x;
   const uint8_t* zr = P.z + (int64_t)row * P.ld_bytes;
   const uint8_t* yr = P.y + (int64_t)row * P.ld_bytes;
@@ -175,6 +176,21 @@ __global__ void __launch_bounds__(kThreads) k_row_lse_t(SampleParams P) {
     st[1] = __builtin_amdgcn_logf(sa);  // log2
     st[2] = b;
     st[3] = __builtin_amdgcn_logf(sb);
+  }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) k_row_lse_t(SampleParams P) {
+  // Only rows the verification can read: the first min(n + 1, n_b) rows of block blockIdx.x (the n
+  // verified ones and the row a bonus token would be drawn from), rows blockIdx.y, + gridDim.y, ...
+  const int b = blockIdx.x;
+  const int start = P.offsets[b], end = P.offsets[b + 1];
+  if (start < 0 || end < start || end > P.n_rows) return;
+  const int nb = end - start;
+  const int m = min(min(max(P.L[b], 0), nb) + 1, nb);
+  for (int j = blockIdx.y; j < m; j += gridDim.y) {
+    if (j != (int)blockIdx.y) __syncthreads();  // the previous row is done with `part`
+    row_lse_one<BF16>(P, start + j);
   }
 }
 
@@ -494,9 +510,10 @@ __global__ void __launch_bounds__(kThreads) k_sample_pick(SampleParams P) {
 hipError_t launch_sample_verify(const SampleParams& p, int in_bf16, hipStream_t s) {
   SampleParams q = p;
   void* args[] = {&q};
-  if (p.n_rows > 0) {
+  if (p.n_rows > 0 && p.n_blocks > 0) {
+    // one workgroup per (block, row slot): a block of up to kRowSlots rows needs one pass
     void* fn = in_bf16 ? (void*)k_row_lse_t<true> : (void*)k_row_lse_t<false>;
-    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.n_rows), dim3(kThreads), args, 0, s);
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.n_blocks, kRowSlots), dim3(kThreads), args, 0, s);
     if (e != hipSuccess) return e;
   }
   // blocks in batches whose slice sums fit the workspace

@@ -188,8 +188,10 @@ opd_status_t opd_length_head_loss(const int32_t* target_top1, const int32_t* dra
  *   row_lse          [n_rows][4] f32 out: (c_z, l_z, c_y, l_y) with log2 sum_v 2^(z_v log2(e) / T) =
  *                    c_z + l_z (c_z a reference near the row maximum, l_z = log2 of the sum relative to
  *                    it), likewise for y; so log of the normaliser of softmax(z / T) is (c_z + l_z) ln 2.
- * Every row's row_lse is computed (one read of z and y); the decisions then read two elements per
- * verified row, and each draw reads its row once more. Decisions and draws are taken in fp32 on sums
+ *                    Written only for the rows the verification can read: the first
+ *                    min(n + 1, n_b) rows of every well-formed block; other entries are left as they are.
+ * Those rows are read once (z and y) for row_lse; the decisions then read two elements per verified
+ * row, and each draw reads its row once more. Decisions and draws are taken in fp32 on sums
  * formed in a fixed order (deterministic); a draw whose target falls on a rounding edge takes the last
  * positive weight before it. Negative L and malformed offsets raise the greedy call's flags.
  * Errors: OPD_ERR_NULL, OPD_ERR_SHAPE, OPD_ERR_DTYPE, OPD_ERR_ALIGN, OPD_ERR_PARAM (temperature),
