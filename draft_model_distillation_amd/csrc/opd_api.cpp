@@ -24,7 +24,6 @@ static_assert(OPD_FLAG_BAD_TOKEN == opd::kFlagBadToken, "flag mismatch");
 namespace {
 
 thread_local std::string g_last_error;
-std::atomic<uint32_t> g_flag_epoch{16};
 std::atomic<uint32_t> g_spin_limit{0};
 
 constexpr int64_t kMaxVocab = 1 << 19;  // 524,288 logits per row
@@ -154,14 +153,6 @@ opd_status_t plan(int mode, int in_bf16, int out_bf16, int64_t n_rows, int64_t v
   return OPD_OK;
 }
 
-uint32_t reserve_flags(uint32_t count) {
-  while (true) {
-    uint32_t base = g_flag_epoch.fetch_add(count);
-    // skip ranges that contain 0 (a freshly zeroed workspace holds flag 0)
-    if ((uint64_t)base + count <= 0xffffffffull && base != 0) return base;
-  }
-}
-
 uint32_t spin_limit() {
   uint32_t v = g_spin_limit.load();
   return v ? v : opd::kDefaultSpinLimit;
@@ -201,7 +192,7 @@ opd_status_t run_team(int mode, const void* z, const void* y, opd_dtype_t dt, in
   p.flags = static_cast<uint32_t*>(ws);
   const int64_t iters = (n_rows + g.n_teams - 1) / g.n_teams;
   if (2 * iters + 2 > 0x7fffffff) return fail(OPD_ERR_SHAPE, "too many rows");
-  p.flag_base = reserve_flags((uint32_t)(2 * iters + 2));
+  p.flag_count = (uint32_t)(2 * iters + 2);
   p.spin_limit = spin_limit();
   hipError_t e = opd::launch_team(p, mode, in_bf16, out_bf16, g.K, g.grid, stream);
   if (e != hipSuccess) return hip_fail(e, "team kernel launch");

@@ -15,8 +15,12 @@ constexpr int kThreads = 256;  // workgroup size of every row kernel (4 wave64)
 constexpr int kStage1Units = 7;
 constexpr int kStage2Units = 2;
 constexpr int kMaxGrid = 4096;  // upper bound on co-resident workgroups the workspace is sized for
-// Workspace layout: [0, 256) header (flag word at offset 0), then the exchange units.
+// Workspace layout: [0, 256) header, then the exchange units. The header holds the sticky flag word
+// (byte 0), the exchange-flag epoch (byte 64) and the count of row-team workgroups that finished the
+// current launch (byte 128), each on its own cache line. A zero-filled header is the initial state.
 constexpr size_t kHeaderBytes = 256;
+constexpr int kEpochWord = 16;  // uint32 index of the epoch in the header
+constexpr int kDoneWord = 32;   // uint32 index of the finished-workgroup count
 constexpr size_t kUnitBytesPerWg = 2 * 8 * 8;  // two stages x up to 8 units x 8 bytes
 constexpr size_t kWorkspaceBytes = kHeaderBytes + (size_t)kMaxGrid * kUnitBytesPerWg;
 
@@ -51,8 +55,8 @@ struct TeamParams {
   uint8_t* dz;
   int64_t ld_dz_bytes;
   uint64_t* units;  // exchange units [n_teams][2][G][8]
-  uint32_t* flags;  // sticky flag word
-  uint32_t flag_base;
+  uint32_t* flags;  // workspace header: sticky flag word, epoch (kEpochWord), done count (kDoneWord)
+  uint32_t flag_count;  // exchange flags this launch takes from the epoch (2 per row iteration + 2)
   uint32_t spin_limit;
 };
 

@@ -287,6 +287,7 @@ struct Shared {
   float wza[4];      // z at the wave's argmax of y
   float row[12];     // row constants, written by wave 0
   int err;
+  uint32_t fbase;    // first exchange flag of this launch
 };
 
 // Row constants in Shared::row.
@@ -533,7 +534,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
   const bool tail_chunk = (cv0 + clen0 == P.nvec) && (P.nvec * EPV != P.vocab);
   uint64_t* const units1 = P.units + (size_t)team * 2 * G * 8;
   uint64_t* const units2 = units1 + (size_t)G * 8;
-  if (tid == 0) sh.err = 0;
+  // Exchange flags come from the epoch in the workspace header, which the previous launch on this
+  // workspace advanced when its last workgroup finished: every launch (also a replay of a captured
+  // graph, whose kernel arguments are frozen) uses flags no earlier launch left in the units. Flags
+  // are epoch + 1 .. epoch + flag_count; the epoch restarts at 0 rather than let a range wrap past 0,
+  // the flag of a zero-filled unit.
+  if (tid == 0) {
+    const uint32_t e = __hip_atomic_load(P.flags + kEpochWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.err = 0;
+    sh.fbase = ((uint64_t)e + P.flag_count + 1u > 0xffffffffull ? 0u : e) + 1u;
+  }
 
   int iter = 0;
   for (int row = team; row < P.n_rows; row += P.n_teams, ++iter) {
@@ -743,7 +753,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
 
     // ---- exchange 1: wave 0 publishes the chunk values, gathers the members' values and forms the
     // row constants; the other waves wait at the barrier
-    const uint32_t flag1 = pp->flag_base + 2u * (uint32_t)iter;
+    const uint32_t flag1 = sh.fbase + 2u * (uint32_t)iter;
     if (wave == 0) {
       {
         const float sz = (sh.wred[0][z0 + 2] + sh.wred[1][z0 + 2]) + (sh.wred[2][z0 + 2] + sh.wred[3][z0 + 2]);
@@ -972,7 +982,19 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       }
     }
   }
-  if (sh.err && tid == 0) atomicOr(P.flags, (uint32_t)kFlagSpinTimeout);
+  if (tid == 0) {
+    if (sh.err) atomicOr(P.flags, (uint32_t)kFlagSpinTimeout);
+    // The last workgroup to finish advances the epoch for the next launch: by then every workgroup
+    // of this launch has read it. Relaxed agent-scope atomics; the kernel boundary orders them
+    // before the next launch's read.
+    const uint32_t grid = (uint32_t)(P.n_teams * P.G);
+    const uint32_t done = __hip_atomic_fetch_add(P.flags + kDoneWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done + 1u == grid) {
+      __hip_atomic_store(P.flags + kDoneWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(P.flags + kEpochWord, (sh.fbase - 1u) + P.flag_count, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- streaming backward

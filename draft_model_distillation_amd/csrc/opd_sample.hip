@@ -393,7 +393,13 @@ __global__ void __launch_bounds__(kThreads) k_sample_pick(SampleParams P) {
   }
   const int n_tiles = (P.nvec + 63) / 64;
   DrawRow d = draw_row<BF16>(P, o.row, o.kind);
-  if (tid < kSampleSlices) ssum[tid] = P.slices[(int64_t)blockIdx.x * kSampleSlices + tid];
+  if (tid < kSampleSlices) {
+    float* const slot = P.slices + (int64_t)blockIdx.x * kSampleSlices + tid;
+    ssum[tid] = *slot;
+    // The slice sums share the workspace with the row-team kernel's exchange units; zeros there read
+    // as units holding flag 0, which no exchange ever waits for.
+    *slot = 0.f;
+  }
   __syncthreads();
   float total = 0.f;
   for (int s = 0; s < kSampleSlices; ++s) total += ssum[s];
