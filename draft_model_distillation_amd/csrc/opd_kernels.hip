@@ -27,13 +27,15 @@
 // The kernel is VALU-heavy for an HBM stream (about 33 VALU instructions per element, 3.5 of them
 // exponentials), so the per-element work is kept minimal and the per-row work (reductions,
 // exchanges, row constants) runs once per workgroup in wave 0 while the other waves wait at
-// barriers and the SIMDs serve the other resident workgroups. A row in an exchange holds up all G
-// members of its team, so from the chunk reductions to the end of each exchange the waves raise
-// their issue priority above the streaming phases of the other workgroups on the CU. Exchanges use 8-byte [value | flag] units written and
-// polled with agent-scope relaxed atomics (sc1: coherent across XCDs without L2 writeback /
-// invalidate); the flag is unique per launch, row iteration and stage, so nothing has to be reset
-// between launches and a stale unit can never be taken for a fresh one. Every wait is bounded and
-// raises a sticky flag instead of hanging.
+// barriers and the SIMDs serve the other resident workgroups. The waves of a CU's workgroups are in
+// different phases of different rows, and the issue priority of each phase (s_setprio) orders them
+// by how much of the team they hold up: the chunk reductions and both exchanges 3 (all G members
+// of the team wait on them), phase B 2 (it feeds the second exchange), phase C 1 (it ends the row
+// and frees the workgroup for its next loads), the loads and phase A 0. Exchanges use 8-byte
+// [value | flag] units written and polled with agent-scope relaxed atomics (sc1: coherent across
+// XCDs without L2 writeback / invalidate); the flag is unique per launch, row iteration and stage,
+// so nothing has to be reset between launches and a stale unit can never be taken for a fresh one.
+// Every wait is bounded and raises a sticky flag instead of hanging.
 
 // Numerics: fp32 throughout with fixed reduction orders (bitwise deterministic). Per row, with
 // M = max z, S_z = sum_v e^(z_v - M), delta = LSE(z) - LSE(y), t_v = p_v (z_v - y_v - delta):
@@ -548,6 +550,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
   int iter = 0;
   for (int row = team; row < P.n_rows; row += P.n_teams, ++iter) {
     __syncthreads();  // the previous row is done with ylds and sh
+    __builtin_amdgcn_s_setprio(0);  // loads and phase A: the lowest issue priority
     // Kernel arguments are re-read (scalar loads) in every row instead of occupying scalar registers
     // for the whole loop.
     KParams* pp = (KParams*)__builtin_amdgcn_kernarg_segment_ptr();
@@ -671,9 +674,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
 
     // ---- chunk maxima
     // From here to the end of the first exchange this team's row is on the critical path of all
-    // K work-groups of the team: the waves take a higher issue priority than the streaming
-    // phases of the other work-groups sharing the CU, and drop it once the row constants arrive.
-    __builtin_amdgcn_s_setprio(2);
+    // G workgroups of the team: the waves take the highest issue priority, above every phase of
+    // the other workgroups sharing the CU, and drop it once the row constants arrive.
+    __builtin_amdgcn_s_setprio(3);
     {
       const float a = wmax(lzmax), c = wmax(lymax);
       if (ln == 0) {
@@ -860,9 +863,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       rc.init(Mz, ln_sz, delta);
 
       // ---- phase B: vectors that pass the bound use their phase-A sums, the rest (near the peak)
-      // are summed element by element. Phase B feeds the second exchange: it runs above the
-      // streaming priority, and the reduction and exchange above that.
-      __builtin_amdgcn_s_setprio(1);
+      // are summed element by element. Phase B feeds the second exchange: it runs above phases A
+      // and C, and the reduction and exchange above that.
+      __builtin_amdgcn_s_setprio(2);
       float pe = 0.f, pb = 0.f, s_slow = 0.f, r_slow = 0.f;
       uint32_t slowbits = 0;
 #pragma unroll
@@ -893,7 +896,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
           fence_vals(r_slow, s_slow);
         }
       }
-      __builtin_amdgcn_s_setprio(2);
+      __builtin_amdgcn_s_setprio(3);
       {
         const float a = wsum(__builtin_fmaf(1.f - delta, pe, pb) + s_slow);
         const float c = wsum(__builtin_fmaf(-delta, pe, pb) + r_slow);
@@ -947,7 +950,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         }
       }
       __syncthreads();
-      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(1);  // phase C: above the loads and phase A of other workgroups
       if (sh.err) break;
 
       if constexpr (MODE == kFused) {
