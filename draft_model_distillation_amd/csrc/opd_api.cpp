@@ -25,6 +25,7 @@ namespace {
 
 thread_local std::string g_last_error;
 std::atomic<uint32_t> g_spin_limit{0};
+std::atomic<uint32_t> g_flag_next{0};  // host-chosen exchange flags: offsets into [2^31, 2^32)
 
 constexpr int64_t kMaxVocab = 1 << 19;  // 524,288 logits per row
 
@@ -87,12 +88,12 @@ opd_status_t check_blocks(const opd_blocks_t* blocks, bool required) {
 // Occupancy (workgroups per CU) of each team-kernel variant and the CU count, per device.
 struct DeviceInfo {
   int cus = 0;
-  int occ[3][2][2][2] = {};  // mode, in_bf16, out_bf16, K index
+  int occ[3][2][2][2][2] = {};  // mode, in_bf16, out_bf16, K index, device-epoch flags
 };
 std::mutex g_dev_mu;
 DeviceInfo g_dev[64];
 
-opd_status_t device_info(int mode, int in_bf16, int out_bf16, int kidx, int K, int* cus, int* occ) {
+opd_status_t device_info(int mode, int in_bf16, int out_bf16, int kidx, int K, int dev_flags, int* cus, int* occ) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -105,10 +106,10 @@ opd_status_t device_info(int mode, int in_bf16, int out_bf16, int kidx, int K, i
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     d.cus = n;
   }
-  int& o = d.occ[mode][in_bf16][out_bf16][kidx];
+  int& o = d.occ[mode][in_bf16][out_bf16][kidx][dev_flags];
   if (o == 0) {
     int n = 0;
-    e = opd::team_occupancy(mode, in_bf16, out_bf16, K, &n);
+    e = opd::team_occupancy(mode, in_bf16, out_bf16, K, dev_flags != 0, &n);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     if (n <= 0) return fail(OPD_ERR_HIP, "kernel cannot be resident");
     o = n;
@@ -124,7 +125,7 @@ struct Geometry {
 
 // Split a row of nvec 16-byte vectors over G workgroups of 256 threads x K slots, and choose how
 // many rows (teams) are in flight so that the whole grid is co-resident.
-opd_status_t plan(int mode, int in_bf16, int out_bf16, int64_t n_rows, int64_t vocab, Geometry* g) {
+opd_status_t plan(int mode, int in_bf16, int out_bf16, int dev_flags, int64_t n_rows, int64_t vocab, Geometry* g) {
   const int epv = in_bf16 ? 8 : 4;
   const int nvec = (int)((vocab + epv - 1) / epv);
   const int K = nvec <= opd::kThreads ? 1 : 5;
@@ -137,7 +138,7 @@ opd_status_t plan(int mode, int in_bf16, int out_bf16, int64_t n_rows, int64_t v
   G = (nvec + chunk - 1) / chunk;
   if (G > opd::kMaxTeamSize) return fail(OPD_ERR_SHAPE, "vocab too large for one team");
   int cus = 0, occ = 0;
-  opd_status_t s = device_info(mode, in_bf16, out_bf16, kidx, K, &cus, &occ);
+  opd_status_t s = device_info(mode, in_bf16, out_bf16, kidx, K, dev_flags, &cus, &occ);
   if (s != OPD_OK) return s;
   int64_t capacity = (int64_t)cus * occ;
   if (capacity > opd::kMaxGrid) capacity = opd::kMaxGrid;
@@ -153,6 +154,29 @@ opd_status_t plan(int mode, int in_bf16, int out_bf16, int64_t n_rows, int64_t v
   return OPD_OK;
 }
 
+// Exchange flags for an eager launch: a fresh range in [2^31 + 1, 2^32), disjoint from the device
+// epoch's range [1, 2^31) that captured launches use, so the two kinds never take each other's
+// units for their own.
+uint32_t reserve_host_flags(uint32_t count) {
+  while (true) {
+    const uint32_t off = g_flag_next.fetch_add(count);
+    if ((uint64_t)off + count < 0x80000000ull) return 0x80000000u + off;
+    uint32_t expected = off + count;  // wrap: restart the offsets (the first caller past the end does)
+    g_flag_next.compare_exchange_strong(expected, 0u);
+  }
+}
+
+// True unless the stream is known not to be capturing: a captured launch takes its flags from the
+// device epoch (kernel arguments are frozen for every replay of a graph).
+bool stream_may_be_captured(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return st != hipStreamCaptureStatusNone;
+}
+
 uint32_t spin_limit() {
   uint32_t v = g_spin_limit.load();
   return v ? v : opd::kDefaultSpinLimit;
@@ -165,8 +189,10 @@ opd_status_t run_team(int mode, const void* z, const void* y, opd_dtype_t dt, in
   if (n_rows == 0) return OPD_OK;
   const int in_bf16 = dt == OPD_BF16;
   const int out_bf16 = (mode == opd::kFused && dz_dt == OPD_BF16) ? 1 : 0;
+  // a launch that may be captured into a graph takes its exchange flags from the workspace epoch
+  const int dev_flags = stream_may_be_captured(stream) ? 1 : 0;
   Geometry g;
-  opd_status_t s = plan(mode, in_bf16, out_bf16, n_rows, vocab, &g);
+  opd_status_t s = plan(mode, in_bf16, out_bf16, dev_flags, n_rows, vocab, &g);
   if (s != OPD_OK) return s;
   opd::TeamParams p;
   std::memset(&p, 0, sizeof(p));
@@ -191,8 +217,9 @@ opd_status_t run_team(int mode, const void* z, const void* y, opd_dtype_t dt, in
   p.units = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ws) + opd::kHeaderBytes);
   p.flags = static_cast<uint32_t*>(ws);
   const int64_t iters = (n_rows + g.n_teams - 1) / g.n_teams;
-  if (2 * iters + 2 > 0x7fffffff) return fail(OPD_ERR_SHAPE, "too many rows");
+  if (2 * iters + 2 > 0x3fffffff) return fail(OPD_ERR_SHAPE, "too many rows");
   p.flag_count = (uint32_t)(2 * iters + 2);
+  p.flag_base = dev_flags ? 0u : reserve_host_flags(p.flag_count);
   p.spin_limit = spin_limit();
   hipError_t e = opd::launch_team(p, mode, in_bf16, out_bf16, g.K, g.grid, stream);
   if (e != hipSuccess) return hip_fail(e, "team kernel launch");

@@ -56,7 +56,8 @@ struct TeamParams {
   int64_t ld_dz_bytes;
   uint64_t* units;  // exchange units [n_teams][2][G][8]
   uint32_t* flags;  // workspace header: sticky flag word, epoch (kEpochWord), done count (kDoneWord)
-  uint32_t flag_count;  // exchange flags this launch takes from the epoch (2 per row iteration + 2)
+  uint32_t flag_count;  // exchange flags this launch uses (2 per row iteration + 2)
+  uint32_t flag_base;   // first flag minus 1, chosen by the host (>= 2^31); 0: from the workspace epoch
   uint32_t spin_limit;
 };
 
@@ -132,7 +133,8 @@ struct SampleParams {
 // in_bf16: 1 if z/y are bf16 (else fp32); out_bf16: 1 if dz is bf16 (else fp32); K: slots/thread.
 hipError_t launch_team(const TeamParams& p, int mode, int in_bf16, int out_bf16, int K, int grid,
                        hipStream_t s);
-hipError_t team_occupancy(int mode, int in_bf16, int out_bf16, int K, int* blocks_per_cu);
+// dev_flags: the instantiation that takes its exchange flags from the workspace epoch (flag_base 0).
+hipError_t team_occupancy(int mode, int in_bf16, int out_bf16, int K, bool dev_flags, int* blocks_per_cu);
 hipError_t launch_bwd(const BwdParams& p, int in_bf16, int out_bf16, hipStream_t s);
 hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, size_t count, hipStream_t s);

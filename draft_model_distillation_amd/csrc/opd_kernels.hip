@@ -512,7 +512,7 @@ __device__ __forceinline__ int first_eq(const float (&v)[EPV], float m) {
 
 typedef __attribute__((address_space(4))) const TeamParams KParams;
 
-template <class In, bool OutBF16, int K, int MODE>
+template <class In, bool OutBF16, int K, int MODE, bool DevFlags>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(In::kWavesPerEU))) k_team(TeamParams P) {
   constexpr int EPV = In::EPV;
   constexpr int VB = EPV * (OutBF16 ? 2 : 4);  // dz bytes per input vector
@@ -536,15 +536,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
   const bool tail_chunk = (cv0 + clen0 == P.nvec) && (P.nvec * EPV != P.vocab);
   uint64_t* const units1 = P.units + (size_t)team * 2 * G * 8;
   uint64_t* const units2 = units1 + (size_t)G * 8;
-  // Exchange flags come from the epoch in the workspace header, which the previous launch on this
-  // workspace advanced when its last workgroup finished: every launch (also a replay of a captured
-  // graph, whose kernel arguments are frozen) uses flags no earlier launch left in the units. Flags
-  // are epoch + 1 .. epoch + flag_count; the epoch restarts at 0 rather than let a range wrap past 0,
-  // the flag of a zero-filled unit.
+  // Exchange flags are base + 1 .. base + flag_count. An eager call gets its range from the host
+  // (flag_base, flags >= 2^31). A call captured into a graph, whose kernel arguments are frozen for
+  // every replay, runs the DevFlags instantiation, which takes the range from the epoch in the
+  // workspace header instead (flags < 2^31); the previous device-flag launch on this workspace
+  // advanced it when its last workgroup finished. Either way no launch uses a flag an earlier one
+  // left in the units; the epoch restarts at 0 rather than let a range pass 2^31 - 1.
   if (tid == 0) {
-    const uint32_t e = __hip_atomic_load(P.flags + kEpochWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t b = P.flag_base;
+    if constexpr (DevFlags) {
+      const uint32_t e = __hip_atomic_load(P.flags + kEpochWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      b = (uint64_t)e + P.flag_count + 1u > 0x7fffffffull ? 0u : e;
+    }
     sh.err = 0;
-    sh.fbase = ((uint64_t)e + P.flag_count + 1u > 0xffffffffull ? 0u : e) + 1u;
+    sh.fbase = b + 1u;
   }
 
   int iter = 0;
@@ -987,15 +992,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
   }
   if (tid == 0) {
     if (sh.err) atomicOr(P.flags, (uint32_t)kFlagSpinTimeout);
-    // The last workgroup to finish advances the epoch for the next launch: by then every workgroup
-    // of this launch has read it. Relaxed agent-scope atomics; the kernel boundary orders them
-    // before the next launch's read.
-    const uint32_t grid = (uint32_t)(P.n_teams * P.G);
-    const uint32_t done = __hip_atomic_fetch_add(P.flags + kDoneWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done + 1u == grid) {
-      __hip_atomic_store(P.flags + kDoneWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(P.flags + kEpochWord, (sh.fbase - 1u) + P.flag_count, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    // Device-mode flags: the last workgroup to finish advances the epoch for the next launch; by
+    // then every workgroup of this launch has read it. Relaxed agent-scope atomics; the kernel
+    // boundary orders them before the next launch's read.
+    if constexpr (DevFlags) {
+      const uint32_t grid = (uint32_t)(P.n_teams * P.G);
+      const uint32_t done = __hip_atomic_fetch_add(P.flags + kDoneWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done + 1u == grid) {
+        __hip_atomic_store(P.flags + kDoneWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(P.flags + kEpochWord, (sh.fbase - 1u) + P.flag_count, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
@@ -1133,37 +1140,43 @@ __global__ void __launch_bounds__(kThreads) k_stream_probe(const uint4* a, const
 
 // ---------------------------------------------------------------- instantiation tables
 
-template <int MODE>
+template <int MODE, bool D>
 void* team_kernel(int in_bf16, int out_bf16, int K) {
   if (MODE != kFused) out_bf16 = 0;
   if (in_bf16) {
-    if (out_bf16) return K == 1 ? (void*)k_team<BF16In, true, 1, MODE> : (void*)k_team<BF16In, true, 5, MODE>;
-    return K == 1 ? (void*)k_team<BF16In, false, 1, MODE> : (void*)k_team<BF16In, false, 5, MODE>;
+    if (out_bf16) return K == 1 ? (void*)k_team<BF16In, true, 1, MODE, D> : (void*)k_team<BF16In, true, 5, MODE, D>;
+    return K == 1 ? (void*)k_team<BF16In, false, 1, MODE, D> : (void*)k_team<BF16In, false, 5, MODE, D>;
   }
-  if (out_bf16) return K == 1 ? (void*)k_team<F32In, true, 1, MODE> : (void*)k_team<F32In, true, 5, MODE>;
-  return K == 1 ? (void*)k_team<F32In, false, 1, MODE> : (void*)k_team<F32In, false, 5, MODE>;
+  if (out_bf16) return K == 1 ? (void*)k_team<F32In, true, 1, MODE, D> : (void*)k_team<F32In, true, 5, MODE, D>;
+  return K == 1 ? (void*)k_team<F32In, false, 1, MODE, D> : (void*)k_team<F32In, false, 5, MODE, D>;
 }
 
-void* team_kernel_any(int mode, int in_bf16, int out_bf16, int K) {
+template <bool D>
+void* team_kernel_mode(int mode, int in_bf16, int out_bf16, int K) {
   switch (mode) {
-    case kFused: return team_kernel<kFused>(in_bf16, out_bf16, K);
-    case kForward: return team_kernel<kForward>(in_bf16, out_bf16, K);
-    default: return team_kernel<kTop1>(in_bf16, out_bf16, K);
+    case kFused: return team_kernel<kFused, D>(in_bf16, out_bf16, K);
+    case kForward: return team_kernel<kForward, D>(in_bf16, out_bf16, K);
+    default: return team_kernel<kTop1, D>(in_bf16, out_bf16, K);
   }
+}
+
+void* team_kernel_any(int mode, int in_bf16, int out_bf16, int K, bool dev_flags) {
+  return dev_flags ? team_kernel_mode<true>(mode, in_bf16, out_bf16, K)
+                   : team_kernel_mode<false>(mode, in_bf16, out_bf16, K);
 }
 
 }  // namespace
 
 hipError_t launch_team(const TeamParams& p, int mode, int in_bf16, int out_bf16, int K, int grid, hipStream_t s) {
-  void* fn = team_kernel_any(mode, in_bf16, out_bf16, K);
+  void* fn = team_kernel_any(mode, in_bf16, out_bf16, K, p.flag_base == 0);
   TeamParams copy = p;
   void* args[] = {&copy};
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
-hipError_t team_occupancy(int mode, int in_bf16, int out_bf16, int K, int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, team_kernel_any(mode, in_bf16, out_bf16, K),
-                                                      kThreads, 0);
+hipError_t team_occupancy(int mode, int in_bf16, int out_bf16, int K, bool dev_flags, int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks_per_cu, team_kernel_any(mode, in_bf16, out_bf16, K, dev_flags), kThreads, 0);
 }
 
 hipError_t launch_bwd(const BwdParams& p, int in_bf16, int out_bf16, hipStream_t s) {

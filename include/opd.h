@@ -38,9 +38,10 @@
  *     numbers but every kernel still terminates.
  *   - A workspace of opd_workspace_size() bytes, zero-filled once when first allocated, must be
  *     passed to every call; calls that share a workspace must not run concurrently. Besides the
- *     sticky flags it holds the state of the cross-workgroup exchanges, including an epoch that
- *     each launch of the row-team kernel reads and advances on the device; kernel arguments carry
- *     no per-call state, so a call captured into a HIP graph may be replayed any number of times.
+ *     sticky flags it holds the state of the cross-workgroup exchanges. A call made while its
+ *     stream is being captured into a HIP graph takes that state from an epoch in the workspace,
+ *     read and advanced on the device by each launch (about 2 us more per launch), so the graph
+ *     may be replayed any number of times; other calls take it from the host.
  *   - Device-side content problems (negative L, malformed offsets, a cross-workgroup wait that
  *     exceeded its bound) set bits in a sticky flag word inside the workspace, read with
  *     opd_read_flags().
