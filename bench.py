@@ -254,6 +254,41 @@ def main():
         write_only_gbs = probe_gbs(None, None, dzb, 1)
         del zb, yb, dzb
 
+    # the separate entry points on the same workload, each timed alone: the forward (loss, top-1s, row
+    # statistics; reads z and y once), the backward from the forward's row statistics (reads z and y,
+    # writes dz) and the verification (top-1s and accept lengths; reads z and y). Algorithmic bytes
+    # per launch beside each.
+    separate = None
+    if not args.profile:
+        esz = 2 if rec.dtype == "bf16" else 4
+        dsz = 2 if dz_dtype == torch.bfloat16 else 4
+
+        def timed(fn):
+            fn()
+            ev0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / args.steps
+
+        fwd_out = opd.opd_loss_fwd(z, y, rec.alpha, rec.tau, ws=ws)
+        fwd_ms = timed(lambda: opd.opd_loss_fwd(z, y, rec.alpha, rec.tau, ws=ws))
+        bwd_ms = timed(lambda: opd.opd_loss_bwd(z, y, rec.alpha, rec.tau, fwd_out[3], fwd_out[1], dz=out["dz"], ws=ws))
+        ver_ms = timed(lambda: opd.verify_accept_len(z, y, off, lens, ws=ws))
+        fwd_b = n * (2 * rec.vocab * esz + 44)
+        bwd_b = n * (rec.vocab * (2 * esz + dsz) + 36)
+        ver_b = n * (2 * rec.vocab * esz + 8)
+        separate = {
+            "opd_loss_fwd": {"ms": fwd_ms, "bytes": fwd_b, "gbs": fwd_b / (fwd_ms * 1e-3) / 1e9},
+            "opd_loss_bwd": {"ms": bwd_ms, "bytes": bwd_b, "gbs": bwd_b / (bwd_ms * 1e-3) / 1e9},
+            "verify_accept_len": {"ms": ver_ms, "bytes": ver_b, "gbs": ver_b / (ver_ms * 1e-3) / 1e9},
+        }
+        del fwd_out
+        if opd.read_flags(ws, clear=True) != 0:
+            print("[bench] device flags raised by the separate entry points", file=sys.stderr)
+            sys.exit(1)
+
     # length-head epilogue (a separate small kernel) on this step's top-1s, one logit per block
     head_us = None
     if not args.profile and len(lens) > 0:
@@ -389,6 +424,8 @@ def main():
         # over this workload's blocks (includes the binding's output allocation), the host packer
         # per call over this workload's requests, and the speculative-sampling verification
         "extras": {"length_head_epilogue_us": head_us, "host_packer_us": pack_us,
+                   # opd_loss_fwd, opd_loss_bwd and verify_accept_len, each per call over the workload
+                   "separate_entry_points": separate,
                    # opd_verify_sample at T = 1 (all kernels) per call; gbs = z and y of the rows the
                    # verification reads, once, / time
                    "sampling_verify": sample,

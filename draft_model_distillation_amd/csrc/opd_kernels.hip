@@ -1102,37 +1102,37 @@ __global__ void __launch_bounds__(kThreads) k_fill_u32(uint32_t* dst, uint32_t v
   for (size_t i = block_id_x() * (size_t)kThreads + thread_id(); i < count; i += stride) dst[i] = value;
 }
 
-// Two nontemporal 16-byte reads and one write per vector, grid-stride: the fused path's HBM pattern
-// with no arithmetic, for the achievable-bandwidth figure reported beside the kernels.
-// Bandwidth probe: KIND 0 reads a and b and writes c = a ^ b, KIND 1 only reads a and b (the xor of
-// everything read is stored only if it equals a value the caller passes and never produces, which
-// keeps the loads alive), KIND 2 only writes c. U independent 16-byte vectors per tensor and thread
-// are in flight per step.
+// Bandwidth probe with no arithmetic, for the achievable-bandwidth figures reported beside the
+// kernels: KIND 0 reads a and b and writes c = a ^ b (the fused path's two reads and one write per
+// 16-byte vector), KIND 1 only reads a and b (the xor of everything read is stored only if it equals
+// a value the caller passes and never produces, which keeps the loads alive), KIND 2 only writes c.
+// One-shot workgroups, each streaming U * 256 consecutive vectors per tensor with U vectors per
+// tensor in flight per thread: in a sweep on MI355X this shape streamed faster for all three
+// patterns than persistent grid-stride loops over 256 to 8192 workgroups.
 template <int KIND, int U>
 __global__ void __launch_bounds__(kThreads) k_stream_probe(const uint4* a, const uint4* b, uint8_t* c, size_t n,
-                                                           size_t stride, uint32_t never) {
+                                                           uint32_t never) {
   uint32_t acc = 0;
-  for (size_t base = block_id_x() * (size_t)kThreads + thread_id(); base < n; base += stride * U) {
-    uint4 x[U], y[U];
+  const size_t v0 = (size_t)block_id_x() * (kThreads * U) + thread_id();
+  uint4 x[U], y[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const size_t i = base + u * stride;
-      if (KIND != 2 && i < n) {
-        x[u] = load_nt(a + i);
-        y[u] = load_nt(b + i);
-      }
+  for (int u = 0; u < U; ++u) {
+    const size_t i = v0 + (size_t)u * kThreads;
+    if (KIND != 2 && i < n) {
+      x[u] = load_nt(a + i);
+      y[u] = load_nt(b + i);
     }
+  }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const size_t i = base + u * stride;
-      if (i >= n) continue;
-      if constexpr (KIND == 0) {
-        store_nt(c + 16 * i, x[u].x ^ y[u].x, x[u].y ^ y[u].y, x[u].z ^ y[u].z, x[u].w ^ y[u].w);
-      } else if constexpr (KIND == 1) {
-        acc ^= (x[u].x ^ y[u].x) ^ (x[u].y ^ y[u].y) ^ (x[u].z ^ y[u].z) ^ (x[u].w ^ y[u].w);
-      } else {
-        store_nt(c + 16 * i, (uint32_t)i, (uint32_t)(i >> 32), 0u, 0u);
-      }
+  for (int u = 0; u < U; ++u) {
+    const size_t i = v0 + (size_t)u * kThreads;
+    if (i >= n) continue;
+    if constexpr (KIND == 0) {
+      store_nt(c + 16 * i, x[u].x ^ y[u].x, x[u].y ^ y[u].y, x[u].z ^ y[u].z, x[u].w ^ y[u].w);
+    } else if constexpr (KIND == 1) {
+      acc ^= (x[u].x ^ y[u].x) ^ (x[u].y ^ y[u].y) ^ (x[u].z ^ y[u].z) ^ (x[u].w ^ y[u].w);
+    } else {
+      store_nt(c + 16 * i, (uint32_t)i, (uint32_t)(i >> 32), 0u, 0u);
     }
   }
   if (KIND == 1 && acc == never && c) store_nt(c, acc, 0u, 0u, 0u);
@@ -1199,23 +1199,22 @@ hipError_t launch_accept(const AcceptParams& p, hipStream_t s) {
 
 hipError_t launch_stream_probe(const void* a, const void* b, void* c, size_t n_vec, hipStream_t s) {
   if (n_vec == 0) return hipSuccess;
-  // Grid sizes and unroll factors that streamed fastest for each pattern in a sweep on MI355X
-  // (grids of 256 to 8192 work-groups, 1 to 8 vectors in flight per tensor and thread).
+  // two vectors per tensor in flight per thread: the fastest of 1, 2, 4 and 8 for the read-read-write
+  // pattern in the sweep (4 was within 1 %, 8 slower); read-only and write-only streams use the same
+  constexpr int U = 2;
   const int kind = (a && b && c) ? 0 : (a && b) ? 1 : 2;
-  const size_t cap = kind == 1 ? 1024 : kind == 2 ? 256 : 512;
-  size_t blocks = (n_vec + kThreads - 1) / kThreads;
-  if (blocks > cap) blocks = cap;
-  const size_t stride = blocks * (size_t)kThreads;
+  const size_t blocks = (n_vec + (size_t)kThreads * U - 1) / ((size_t)kThreads * U);
+  if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
   const uint4* pa = (const uint4*)a;
   const uint4* pb = (const uint4*)b;
   uint8_t* pc = (uint8_t*)c;
   if (kind == 0)
-    hipLaunchKernelGGL((k_stream_probe<0, 1>), dim3((unsigned)blocks), dim3(kThreads), 0, s, pa, pb, pc, n_vec, stride, 0u);
+    hipLaunchKernelGGL((k_stream_probe<0, U>), dim3((unsigned)blocks), dim3(kThreads), 0, s, pa, pb, pc, n_vec, 0u);
   else if (kind == 1)
-    hipLaunchKernelGGL((k_stream_probe<1, 4>), dim3((unsigned)blocks), dim3(kThreads), 0, s, pa, pb, pc, n_vec, stride,
+    hipLaunchKernelGGL((k_stream_probe<1, U>), dim3((unsigned)blocks), dim3(kThreads), 0, s, pa, pb, pc, n_vec,
                        0x9e3779b9u);
   else
-    hipLaunchKernelGGL((k_stream_probe<2, 4>), dim3((unsigned)blocks), dim3(kThreads), 0, s, pa, pb, pc, n_vec, stride, 0u);
+    hipLaunchKernelGGL((k_stream_probe<2, U>), dim3((unsigned)blocks), dim3(kThreads), 0, s, pa, pb, pc, n_vec, 0u);
   return hipGetLastError();
 }
 
