@@ -96,3 +96,49 @@ def test_graph_replays_match_eager(lib):
         for k, v in ref[(idx + 1) % 3].items():
             assert torch.equal(e[k], v), (step, "eager", k)
     assert m.read_flags(clear=True) == 0
+
+
+def test_graph_of_separate_calls_replays_match_eager(lib):
+    """Forward, backward from its row statistics and verification, captured together in one graph."""
+    import torch
+
+    m = lib
+    off = torch.arange(0, ROWS + 1, 16, dtype=torch.int32, device="cuda")
+    lens = torch.full((ROWS // 16,), 9, dtype=torch.int32, device="cuda")
+    alpha, tau = 0.7, 0.02
+    inputs = [_inputs(s) for s in (21, 22)]
+
+    def eager(z, y):
+        loss, a, d, stats = m.opd_loss_fwd(z, y, alpha, tau)
+        dz = m.opd_loss_bwd(z, y, alpha, tau, stats, a)
+        a2, d2, acc = m.verify_accept_len(z, y, off, lens)
+        return {"loss": loss, "a": a, "d": d, "stats": stats, "dz": dz, "a2": a2, "d2": d2, "acc": acc}
+
+    _say("separate calls: eager references")
+    ref = [eager(z, y) for z, y in inputs]
+    torch.cuda.synchronize()
+    assert m.read_flags(clear=True) == 0
+
+    zs, ys = torch.empty_like(inputs[0][0]), torch.empty_like(inputs[0][1])
+    zs.copy_(inputs[0][0])
+    ys.copy_(inputs[0][1])
+    eager(zs, ys)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    _say("separate calls: capture")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = eager(zs, ys)
+    torch.cuda.synchronize()
+    for step, idx in enumerate([1, 0, 0, 1]):
+        zs.copy_(inputs[idx][0])
+        ys.copy_(inputs[idx][1])
+        graph.replay()
+        torch.cuda.synchronize()
+        _say(f"separate calls: replay {step} on inputs {idx}")
+        for k, v in ref[idx].items():
+            assert torch.equal(out[k], v), (step, idx, k)
+        e = eager(*inputs[1 - idx])
+        torch.cuda.synchronize()
+        for k, v in ref[1 - idx].items():
+            assert torch.equal(e[k], v), (step, "eager", k)
+    assert m.read_flags(clear=True) == 0

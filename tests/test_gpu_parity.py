@@ -200,6 +200,11 @@ def test_full_size_fused(lib, name, nsample):
     torch.cuda.synchronize()
     assert torch.equal(dz, out["dz"])
     del dz
+    a2, d2, acc = lib.verify_accept_len(z, y, off, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(a2, out["target_top1"]) and torch.equal(d2, out["draft_top1"])
+    assert torch.equal(acc, out["accept_len"])
+    assert lib.read_flags(clear=True) == 0
 
 
 # ------------------------------------------------------------------ edge cases
