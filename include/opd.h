@@ -228,8 +228,9 @@ opd_status_t opd_verify_sample(const void* z, const void* y, opd_dtype_t dt, int
  *   scratch    caller device memory of at least opd_lmhead_scratch_size(min(chunk_rows, n_rows),
  *              vocab, ld_y) bytes, 16-byte aligned: one chunk of fp32 logits and of bf16 dz.
  * dh and dW are formed from the bf16-rounded dz of the row kernel. The three products go through
- * rocBLAS, which keeps one handle (and its own device workspace) per device for the process; the
- * handle has atomics disabled, so results are deterministic.
+ * rocBLAS, which keeps one handle (and its own device workspace) per device for the process,
+ * created (with a device allocation) on the first call on a device; the handle has atomics
+ * disabled, so results are deterministic. This call is not tested under stream capture.
  * Errors: OPD_ERR_NULL, OPD_ERR_SHAPE, OPD_ERR_DTYPE (dt_y not OPD_F32), OPD_ERR_ALIGN,
  * OPD_ERR_PARAM, OPD_ERR_WORKSPACE (ws or scratch too small), OPD_ERR_HIP (including rocBLAS errors).
  */
