@@ -88,7 +88,7 @@ opd_status_t check_blocks(const opd_blocks_t* blocks, bool required) {
 // Occupancy (workgroups per CU) of each team-kernel variant and the CU count, per device.
 struct DeviceInfo {
   int cus = 0;
-  int occ[3][2][2][2][2] = {};  // mode, in_bf16, out_bf16, K index, device-epoch flags
+  int occ[3][2][2][3][2] = {};  // mode, in_bf16, out_bf16, K index (1, 3, 5), device-epoch flags
 };
 std::mutex g_dev_mu;
 DeviceInfo g_dev[64];
@@ -123,13 +123,10 @@ struct Geometry {
   int K, G, chunk_vec, nvec, n_teams, grid;
 };
 
-// Split a row of nvec 16-byte vectors over G workgroups of 256 threads x K slots, and choose how
-// many rows (teams) are in flight so that the whole grid is co-resident.
-opd_status_t plan(int mode, int in_bf16, int out_bf16, int dev_flags, int64_t n_rows, int64_t vocab, Geometry* g) {
-  const int epv = in_bf16 ? 8 : 4;
-  const int nvec = (int)((vocab + epv - 1) / epv);
-  const int K = nvec <= opd::kThreads ? 1 : 5;
-  const int kidx = K == 1 ? 0 : 1;
+// Split a row of nvec 16-byte vectors over G workgroups of 256 threads x K slots each, and choose
+// how many rows (teams) are in flight so that the whole grid is co-resident.
+opd_status_t plan_k(int mode, int in_bf16, int out_bf16, int dev_flags, int K, int nvec, int64_t n_rows, Geometry* g) {
+  const int kidx = K == 1 ? 0 : K == 3 ? 1 : 2;
   const int slots = opd::kThreads * K;
   int G = (nvec + slots - 1) / slots;
   int chunk = (nvec + G - 1) / G;
@@ -152,6 +149,20 @@ opd_status_t plan(int mode, int in_bf16, int out_bf16, int dev_flags, int64_t n_
   g->n_teams = (int)teams;
   g->grid = (int)(teams * G);
   return OPD_OK;
+}
+
+// Five slots per thread (the fewest workgroups per row, so the most rows in flight) unless a whole
+// batch fits the teams of the three-slot plan at once: then every row starts immediately either
+// way, and the shorter chunks finish sooner (a 16-row decode at V = 151,936: 14.3 against 15.1 us
+// per call). Rows of at most 256 vectors take one slot per thread.
+opd_status_t plan(int mode, int in_bf16, int out_bf16, int dev_flags, int64_t n_rows, int64_t vocab, Geometry* g) {
+  const int epv = in_bf16 ? 8 : 4;
+  const int nvec = (int)((vocab + epv - 1) / epv);
+  if (nvec <= opd::kThreads) return plan_k(mode, in_bf16, out_bf16, dev_flags, 1, nvec, n_rows, g);
+  opd_status_t s = plan_k(mode, in_bf16, out_bf16, dev_flags, 3, nvec, n_rows, g);
+  if (s != OPD_OK) return s;
+  if (g->n_teams >= n_rows) return OPD_OK;
+  return plan_k(mode, in_bf16, out_bf16, dev_flags, 5, nvec, n_rows, g);
 }
 
 // Exchange flags for an eager launch: a fresh range in [2^31 + 1, 2^32), disjoint from the device

@@ -130,7 +130,8 @@ struct SampleParams {
   int32_t block0;  // first block of the current batch
 };
 
-// in_bf16: 1 if z/y are bf16 (else fp32); out_bf16: 1 if dz is bf16 (else fp32); K: slots/thread.
+// in_bf16: 1 if z/y are bf16 (else fp32); out_bf16: 1 if dz is bf16 (else fp32); K: slots per thread
+// (1, 3 or 5).
 hipError_t launch_team(const TeamParams& p, int mode, int in_bf16, int out_bf16, int K, int grid,
                        hipStream_t s);
 // dev_flags: the instantiation that takes its exchange flags from the workspace epoch (flag_base 0).

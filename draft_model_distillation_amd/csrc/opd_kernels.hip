@@ -1140,15 +1140,18 @@ __global__ void __launch_bounds__(kThreads) k_stream_probe(const uint4* a, const
 
 // ---------------------------------------------------------------- instantiation tables
 
+template <class In, bool OutBF16, int MODE, bool D>
+void* team_kernel_k(int K) {
+  return K == 1 ? (void*)k_team<In, OutBF16, 1, MODE, D>
+       : K == 3 ? (void*)k_team<In, OutBF16, 3, MODE, D>
+                : (void*)k_team<In, OutBF16, 5, MODE, D>;
+}
+
 template <int MODE, bool D>
 void* team_kernel(int in_bf16, int out_bf16, int K) {
   if (MODE != kFused) out_bf16 = 0;
-  if (in_bf16) {
-    if (out_bf16) return K == 1 ? (void*)k_team<BF16In, true, 1, MODE, D> : (void*)k_team<BF16In, true, 5, MODE, D>;
-    return K == 1 ? (void*)k_team<BF16In, false, 1, MODE, D> : (void*)k_team<BF16In, false, 5, MODE, D>;
-  }
-  if (out_bf16) return K == 1 ? (void*)k_team<F32In, true, 1, MODE, D> : (void*)k_team<F32In, true, 5, MODE, D>;
-  return K == 1 ? (void*)k_team<F32In, false, 1, MODE, D> : (void*)k_team<F32In, false, 5, MODE, D>;
+  if (in_bf16) return out_bf16 ? team_kernel_k<BF16In, true, MODE, D>(K) : team_kernel_k<BF16In, false, MODE, D>(K);
+  return out_bf16 ? team_kernel_k<F32In, true, MODE, D>(K) : team_kernel_k<F32In, false, MODE, D>(K);
 }
 
 template <bool D>

@@ -266,6 +266,40 @@ def test_vocab_sizes_and_padding(lib, dtype_name, v):
         assert ok, f"row {r}: {msg}"
 
 
+@pytest.mark.parametrize("dtype_name,v", [("bf16", 100003), ("f32", 77777), ("bf16", 151937), ("f32", 151937)])
+def test_batches_past_the_three_slot_plan(lib, dtype_name, v):
+    """120 rows of a wide vocabulary: more rows than the three-slot plan has teams (at most about 90
+    for these widths), so the five-slot plan runs, which the small batches of the other tests here
+    do not reach; ragged vocabularies and padded rows."""
+    import torch
+
+    rng = np.random.default_rng(v + 7)
+    n = 120
+    epv = 8 if dtype_name == "bf16" else 4
+    ld = ((v + epv - 1) // epv) * epv + 2 * epv
+    z, y = _random_rows(rng, n, v, scale=2.5)
+    zt, zx = _to_dev_padded(z, ld, dtype_name)
+    yt, yx = _to_dev_padded(y, ld, dtype_name)
+    _say(f"120 rows vocab {v} {dtype_name} ld={ld}")
+    cuts = [0, 16, 17, 40, 64, 100, n]
+    off = torch.tensor(cuts, dtype=torch.int32, device="cuda")
+    Ls = [16, 1, 30, 5, 0, 12]
+    lens = torch.tensor(Ls, dtype=torch.int32, device="cuda")
+    out = lib.opd_fused_fwd_bwd_verify(zt, yt, off, lens, 0.4, 0.04, dz_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert lib.read_flags(clear=True) == 0
+    a_ref, d_ref = O.top1_rows(yx), O.top1_rows(zx)
+    assert np.array_equal(out["target_top1"].cpu().numpy(), a_ref)
+    assert np.array_equal(out["draft_top1"].cpu().numpy(), d_ref)
+    acc_ref, _ = O.accept_lengths(d_ref, a_ref, cuts, Ls)
+    assert np.array_equal(out["accept_len"].cpu().numpy(), acc_ref)
+    dz = out["dz"].cpu().numpy().astype(np.float64)
+    loss = out["loss"].cpu().numpy()
+    for r in range(0, n, 6):
+        ok, msg = parity.check_row(zx[r], yx[r], 0.4, 0.04, loss[r], dz[r])
+        assert ok, f"row {r}: {msg}"
+
+
 def test_seeded_random_shapes_fused(lib):
     """A fixed seed draws shapes across the launch plans (one to several workgroups per row, a
     partial last vector, padded pitches, fp32 / bf16 in and out, random alpha / tau / weights, random
