@@ -142,3 +142,42 @@ def test_graph_of_separate_calls_replays_match_eager(lib):
         for k, v in ref[1 - idx].items():
             assert torch.equal(e[k], v), (step, "eager", k)
     assert m.read_flags(clear=True) == 0
+
+
+def test_graph_replays_across_the_epoch_wrap(lib):
+    """The epoch of a fresh workspace set just below 2^31 - 1: replays run across the point where the
+    range restarts from 1, and every replay still matches the eager result."""
+    import torch
+
+    m = lib
+    rows = 96  # two row iterations per team at 85 teams: six flags per launch
+    off = torch.arange(0, rows + 1, 16, dtype=torch.int32, device="cuda")
+    lens = torch.full((rows // 16,), 16, dtype=torch.int32, device="cuda")
+    alpha, tau = 0.5, 0.05
+    g = torch.Generator(device="cuda").manual_seed(31)
+    base = torch.randn(rows, VOCAB, device="cuda", generator=g) * 3.0
+    z = (base + torch.randn(rows, VOCAB, device="cuda", generator=g) * 1.5).to(torch.bfloat16)
+    y = base.to(torch.bfloat16)
+    ws = torch.zeros(m.load_library().opd_workspace_size(), dtype=torch.uint8, device="cuda")
+    ref = m.opd_fused_fwd_bwd_verify(z, y, off, lens, alpha, tau, ws=ws)
+    out = {k: torch.empty_like(v) for k, v in ref.items()}
+    m.opd_fused_fwd_bwd_verify(z, y, off, lens, alpha, tau, ws=ws, out=out)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        m.opd_fused_fwd_bwd_verify(z, y, off, lens, alpha, tau, ws=ws, out=out)
+    torch.cuda.synchronize()
+    ws.zero_()  # a fresh workspace whose epoch is 24 below the end of its range
+    ws.view(torch.int32)[16] = 0x7FFFFFFF - 24
+    torch.cuda.synchronize()
+    for step in range(12):
+        for v in out.values():
+            v.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            assert torch.equal(out[k], v), (step, k)
+    epoch = int(ws.view(torch.int32)[16].item())
+    _say(f"epoch after the replays: {epoch}")
+    assert 0 < epoch < 0x7FFFFFFF - 24  # the range restarted during the replays
+    assert m.read_flags(ws, clear=True) == 0
