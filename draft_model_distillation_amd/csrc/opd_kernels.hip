@@ -1077,9 +1077,14 @@ __global__ void __launch_bounds__(kThreads) k_bwd(BwdParams P) {
 
 // ---------------------------------------------------------------- accept length per packed block
 
+// One wave per block: lane j compares row j of each 64-row window of the block, and a ballot gives
+// the first mismatch, so a block costs one round of loads instead of one per accepted row.
+constexpr int kAcceptBlocksPerGroup = kThreads / 64;
+
 __global__ void __launch_bounds__(kThreads) k_accept(AcceptParams P) {
-  const int b = block_id_x() * kThreads + thread_id();
-  if (b >= P.n_blocks) return;
+  const int lane = thread_id() & 63;
+  const int b = block_id_x() * kAcceptBlocksPerGroup + (thread_id() >> 6);
+  if (b >= P.n_blocks) return;  // wave-uniform
   const int start = P.offsets[b], end = P.offsets[b + 1];
   uint32_t fl = 0;
   int acc = 0;
@@ -1092,10 +1097,21 @@ __global__ void __launch_bounds__(kThreads) k_accept(AcceptParams P) {
       lb = 0;
     }
     const int n = min(lb, end - start);
-    while (acc < n && P.draft_top1[start + acc] == P.target_top1[start + acc]) ++acc;
+    acc = n;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+      const int j = j0 + lane;
+      const bool mismatch = j < n && P.draft_top1[start + j] != P.target_top1[start + j];
+      const uint64_t m = __builtin_amdgcn_ballot_w64(mismatch);
+      if (m) {
+        acc = j0 + (int)__builtin_ctzll(m);
+        break;
+      }
+    }
   }
-  P.accept_len[b] = acc;
-  if (fl) atomicOr(P.flags, fl);
+  if (lane == 0) {
+    P.accept_len[b] = acc;
+    if (fl) atomicOr(P.flags, fl);
+  }
 }
 
 __global__ void __launch_bounds__(kThreads) k_fill_u32(uint32_t* dst, uint32_t value, size_t count, size_t stride) {
@@ -1194,7 +1210,7 @@ hipError_t launch_bwd(const BwdParams& p, int in_bf16, int out_bf16, hipStream_t
 }
 
 hipError_t launch_accept(const AcceptParams& p, hipStream_t s) {
-  dim3 grid((p.n_blocks + kThreads - 1) / kThreads);
+  dim3 grid((p.n_blocks + kAcceptBlocksPerGroup - 1) / kAcceptBlocksPerGroup);
   AcceptParams copy = p;
   void* args[] = {&copy};
   return hipLaunchKernel((void*)k_accept, grid, dim3(kThreads), args, 0, s);
