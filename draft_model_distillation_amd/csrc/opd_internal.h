@@ -13,7 +13,7 @@ namespace opd {
 
 constexpr int kThreads = 256;  // workgroup size of every row kernel (4 wave64)
 constexpr int kStage1Units = 7;
-constexpr int kStage2Units = 2;
+constexpr int kStage2Units = 5;  // S, clipped sum, lowest indices of the row maxima of z and y, z at the latter
 constexpr int kMaxGrid = 4096;  // upper bound on co-resident workgroups the workspace is sized for
 // Workspace layout: [0, 256) header, then the exchange units. The header holds the sticky flag word
 // (byte 0), the exchange-flag epoch (byte 64) and the count of row-team workgroups that finished the

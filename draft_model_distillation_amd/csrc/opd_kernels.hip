@@ -17,12 +17,13 @@
 //   phase A  per 16-byte vector: max z, max y, max(z - y), and sums of 2^(z log2e - c) and of the
 //            same terms times (z - y) relative to the vector's own c = fl(max z log2e); one running
 //            sum of 2^(y log2e - r) per lane
-//   chunk    maxima, lowest indices of the maxima, sums rescaled to the chunk maxima
-//   -- exchange 1 --  wave 0 publishes 7 values, gathers all members' and combines them in a fixed
+//   chunk    maxima, sums rescaled to the chunk maxima
+//   -- exchange 1 --  wave 0 publishes 4 values, gathers all members' and combines them in a fixed
 //                     order: every member derives identical row constants
 //   phase B  S and the clipped reverse KL: vectors whose bound is <= tau provably hold no clipped
-//            term and use their phase-A sums; the rest (near the peak) are visited element by element
-//   -- exchange 2 --  the two sums
+//            term and use their phase-A sums; the rest (near the peak) are visited element by element;
+//            then the chunk's lowest indices of the row maxima (decoded only where a lane holds one)
+//   -- exchange 2 --  the two sums, the two indices and z at the target top-1
 //   phase C  dz written once (bf16 rounded to nearest even, or fp32)
 // The kernel is VALU-heavy for an HBM stream (about 33 VALU instructions per element, 3.5 of them
 // exponentials), so the per-element work is kept minimal and the per-row work (reductions,
@@ -501,11 +502,14 @@ __device__ __forceinline__ int first_eq(const float (&v)[EPV], float m) {
 //            terms times (z - y), with c_k = fl(max z log2e); per lane: sum of 2^(y log2e - r) with r
 //            the first vector's fl(max y log2e) (recomputed from the lane maximum if y climbs more
 //            than 96 octaves above it)
-//   chunk    maxima -> lowest indices of the maxima, sums rescaled to the chunk maxima
-//   team     wave 0 publishes the chunk's 7 values, gathers the G members' values and forms the row
+//   chunk    maxima, sums rescaled to the chunk maxima (top-1 mode: the lowest indices of the chunk
+//            maxima instead of sums)
+//   team     wave 0 publishes the chunk's 4 values, gathers the G members' values and forms the row
 //            constants (exchange 1)
-//   phase B  S and the clipped reverse KL (vector bound; element by element near the peak);
-//            wave 0 exchanges the 2 sums (exchange 2) and writes the row outputs (chunk 0)
+//   phase B  S and the clipped reverse KL (vector bound; element by element near the peak), then the
+//            chunk's lowest indices of the row maxima of z and y and z at the latter (kBig where the
+//            chunk does not reach a row maximum: usually only one member of the team decodes);
+//            wave 0 exchanges these 5 values (exchange 2) and writes the row outputs (chunk 0)
 //   phase C  dz of every vector of the chunk
 // Waves other than wave 0 wait at the barriers while wave 0 exchanges: the SIMDs run the other
 // resident workgroups meanwhile.
@@ -706,7 +710,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     }
     int wiz = kBig, wiy = kBig;
     float wza = 0.f;
-    {
+    if constexpr (!kSums) {  // top-1 mode: the chunk's lowest indices of its maxima go into exchange 1
       const bool hz = lzmax == Mzc;
       if (__builtin_amdgcn_ballot_w64(hz)) {  // a wave holding the chunk maximum of z
         int kk = K;
@@ -762,6 +766,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     // ---- exchange 1: wave 0 publishes the chunk values, gathers the members' values and forms the
     // row constants; the other waves wait at the barrier
     const uint32_t flag1 = sh.fbase + 2u * (uint32_t)iter;
+    // values per member in exchange 1: maxima and sums (the top-1 indices follow in exchange 2), or
+    // in top-1 mode the maxima and their lowest indices
+    constexpr int NU1 = kSums ? 4 : kStage1Units;
     if (wave == 0) {
       {
         const float sz = (sh.wred[0][z0 + 2] + sh.wred[1][z0 + 2]) + (sh.wred[2][z0 + 2] + sh.wred[3][z0 + 2]);
@@ -787,8 +794,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         }
       }
       if (G > 1) {
-        publish<kStage1Units>(units1 + (size_t)chunk * 8, ln, flag1, sh.part + z0);
-        if (!gather_wave<kStage1Units>(sh.rx + z0, units1, G, ln, flag1, pp->spin_limit)) sh.err = 1;
+        publish<NU1>(units1 + (size_t)chunk * 8, ln, flag1, sh.part + z0);
+        if (!gather_wave<NU1>(sh.rx + z0, units1, G, ln, flag1, pp->spin_limit)) sh.err = 1;
       }
       float Mz, My, Sz = 0.f, Sy = 0.f, za;
       int dtop, atop;
@@ -797,32 +804,36 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         float mz = kNegInf, my = kNegInf, lsz = 0.f, lsy = 0.f, lza = 0.f;
         int liz = kBig, liy = kBig;
         for (int c = ln; c < G; c += 64) {
-          mz = fmaxf(mz, __uint_as_float(sh.rx[z0 + c * kStage1Units + 0]));
-          my = fmaxf(my, __uint_as_float(sh.rx[z0 + c * kStage1Units + 2]));
+          mz = fmaxf(mz, __uint_as_float(sh.rx[z0 + c * NU1 + 0]));
+          my = fmaxf(my, __uint_as_float(sh.rx[z0 + c * NU1 + 2]));
         }
         Mz = wmax(mz);
         My = wmax(my);
         const float cHz = Mz * kLog2e, cHy = My * kLog2e;
         for (int c = ln; c < G; c += 64) {
-          const uint32_t* u = sh.rx + z0 + c * kStage1Units;
+          const uint32_t* u = sh.rx + z0 + c * NU1;
           const float mzc = __uint_as_float(u[0]), myc = __uint_as_float(u[2]);
           if constexpr (kSums) {
             lsz = __builtin_fmaf(__uint_as_float(u[1]), exp2_fast(mzc * kLog2e - cHz), lsz);
             lsy = __builtin_fmaf(__uint_as_float(u[3]), exp2_fast(myc * kLog2e - cHy), lsy);
-          }
-          if (mzc == Mz) liz = min(liz, (int)u[4]);
-          if (myc == My && (int)u[5] < liy) {
-            liy = (int)u[5];
-            lza = __uint_as_float(u[6]);
+          } else {
+            if (mzc == Mz) liz = min(liz, (int)u[4]);
+            if (myc == My && (int)u[5] < liy) {
+              liy = (int)u[5];
+              lza = __uint_as_float(u[6]);
+            }
           }
         }
         if constexpr (kSums) {
           Sz = wsum(lsz);
           Sy = wsum(lsy);
+          dtop = atop = kBig;  // from exchange 2
+          za = 0.f;
+        } else {
+          dtop = wmin(liz);
+          atop = wmin(liy);
+          za = wsum(liy == atop ? lza : 0.f);
         }
-        dtop = wmin(liz);
-        atop = wmin(liy);
-        za = wsum(liy == atop ? lza : 0.f);
       } else {
         Mz = Mzc;
         My = Myc;
@@ -854,12 +865,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     if (sh.err) break;
 
     const float Mz = sh.row[z0 + kRowMz];
-    const int dtop = __float_as_int(sh.row[z0 + kRowDtop]);
-    const int atop = __float_as_int(sh.row[z0 + kRowAtop]);
     if constexpr (MODE == kTop1) {
       if (chunk == 0 && tid == 0) {
-        pp->target_top1[row] = atop;
-        if (pp->draft_top1) pp->draft_top1[row] = dtop;
+        pp->target_top1[row] = __float_as_int(sh.row[z0 + kRowAtop]);
+        if (pp->draft_top1) pp->draft_top1[row] = __float_as_int(sh.row[z0 + kRowDtop]);
       }
     } else {
       const float ln_sz = sh.row[z0 + kRowLnSz];
@@ -902,12 +911,64 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         }
       }
       __builtin_amdgcn_s_setprio(3);
+      // lowest indices of the row maxima within this chunk (kBig where the chunk does not reach
+      // them), and z at the one of y: only waves holding a row maximum decode, which is usually one
+      // wave of one member of the team
+      int wiz = kBig, wiy = kBig;
+      float wza = 0.f;
+      {
+        const float Myr = sh.row[z0 + kRowMy];
+        int kk = K;
+#pragma unroll
+        for (int k = K - 1; k >= 0; --k) kk = (vmlds[k * kThreads + lt].z() == Mz) ? k : kk;
+        const bool hz = kk < K;
+        if (__builtin_amdgcn_ballot_w64(hz)) {
+          int iz = kBig;
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            if (__builtin_amdgcn_ballot_w64(hz && kk == k)) {
+              if (hz && kk == k) {
+                float x[EPV];
+                In::decode(zr[k], x);
+                iz = (cv0 + lt + k * kThreads) * EPV + first_eq<EPV>(x, Mz);
+              }
+            }
+          }
+          wiz = wmin(iz);
+        }
+        const bool hy = lymax == Myr;
+        if (__builtin_amdgcn_ballot_w64(hy)) {
+          int iy = kBig;
+          float za = 0.f;
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            if (__builtin_amdgcn_ballot_w64(hy && kym == k)) {
+              if (hy && kym == k) {
+                float x[EPV], w[EPV];
+                In::decode(zr[k], x);
+                In::decode(ylds[k * kThreads + lt], w);
+                const int e0 = first_eq<EPV>(w, Myr);
+                float zv = x[0];
+#pragma unroll
+                for (int e = 1; e < EPV; ++e) zv = (e == e0) ? x[e] : zv;
+                iy = (cv0 + lt + k * kThreads) * EPV + e0;
+                za = zv;
+              }
+            }
+          }
+          wiy = wmin(iy);
+          wza = wsum(iy == wiy ? za : 0.f);  // the ln holding the index (unique)
+        }
+      }
       {
         const float a = wsum(__builtin_fmaf(1.f - delta, pe, pb) + s_slow);
         const float c = wsum(__builtin_fmaf(-delta, pe, pb) + r_slow);
         if (ln == 0) {
           sh.wred[wv][z0 + 0] = a;
           sh.wred[wv][z0 + 1] = c;
+          sh.widx[wv][z0 + 0] = wiz;
+          sh.widx[wv][z0 + 1] = wiy;
+          sh.wza[z0 + wv] = wza;
         }
       }
       __syncthreads();
@@ -918,26 +979,52 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         if (ln == 0) {
           sh.part[z0 + 0] = __float_as_uint((sh.wred[0][z0 + 0] + sh.wred[1][z0 + 0]) + (sh.wred[2][z0 + 0] + sh.wred[3][z0 + 0]));
           sh.part[z0 + 1] = __float_as_uint((sh.wred[0][z0 + 1] + sh.wred[1][z0 + 1]) + (sh.wred[2][z0 + 1] + sh.wred[3][z0 + 1]));
+          int ciz = kBig, ciy = kBig;
+          float cza = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            ciz = min(ciz, sh.widx[q][z0 + 0]);
+            if (sh.widx[q][z0 + 1] < ciy) {
+              ciy = sh.widx[q][z0 + 1];
+              cza = sh.wza[z0 + q];
+            }
+          }
+          sh.part[z0 + 2] = (uint32_t)ciz;
+          sh.part[z0 + 3] = (uint32_t)ciy;
+          sh.part[z0 + 4] = __float_as_uint(cza);
         }
         if (G > 1) {
           publish<kStage2Units>(units2 + (size_t)chunk * 8, ln, flag2, sh.part + z0);
           if (need_all && !gather_wave<kStage2Units>(sh.rx + z0, units2, G, ln, flag2, pp->spin_limit)) sh.err = 1;
         }
         float S = __uint_as_float(sh.part[z0 + 0]), rkl = __uint_as_float(sh.part[z0 + 1]);
+        int dtop = (int)sh.part[z0 + 2], atop = (int)sh.part[z0 + 3];
+        float za = __uint_as_float(sh.part[z0 + 4]);
         if (G > 1 && need_all) {
-          float ls = 0.f, lr = 0.f;
+          float ls = 0.f, lr = 0.f, lza = 0.f;
+          int liz = kBig, liy = kBig;
           for (int c = ln; c < G; c += 64) {
-            ls += __uint_as_float(sh.rx[z0 + c * kStage2Units + 0]);
-            lr += __uint_as_float(sh.rx[z0 + c * kStage2Units + 1]);
+            const uint32_t* u = sh.rx + z0 + c * kStage2Units;
+            ls += __uint_as_float(u[0]);
+            lr += __uint_as_float(u[1]);
+            liz = min(liz, (int)u[2]);
+            if ((int)u[3] < liy) {
+              liy = (int)u[3];
+              lza = __uint_as_float(u[4]);
+            }
           }
           S = wsum(ls);
           rkl = wsum(lr);
+          dtop = wmin(liz);
+          atop = wmin(liy);
+          za = wsum(liy == atop ? lza : 0.f);
         }
         if (ln == 0) {
           sh.row[z0 + kRowS] = S;
           sh.row[z0 + kRowRkl] = rkl;
+          sh.row[z0 + kRowAtop] = __int_as_float(atop);
           if (chunk == 0) {
-            const float My = sh.row[z0 + kRowMy], ln_sy = sh.row[z0 + kRowLnSy], za = sh.row[z0 + kRowZa];
+            const float My = sh.row[z0 + kRowMy], ln_sy = sh.row[z0 + kRowLnSy];
             const float ce = (Mz - za) + ln_sz;
             float* st = pp->row_stats + 8 * (int64_t)row;
             pp->loss[row] = alpha * rkl + (1.f - alpha) * ce;
@@ -964,7 +1051,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         dc.init(rc, sh.row[z0 + kRowS], alpha, pp->grad_loss ? pp->grad_loss[row] : 1.f);
         const __amdgpu_buffer_rsrc_t rd = rsrc(pp->dz + (int64_t)row * pp->ld_dz_bytes + (int64_t)cv0 * VB, clen * VB);
         __asm__ volatile("" : "+v"(lt));  // fresh offsets: not kept live from the loads
-        // the one vector holding the target top-1 (if it lies in this chunk)
+        // the one vector holding the target top-1 (if it lies in this chunk), from exchange 2
+        const int atop = __float_as_int(sh.row[z0 + kRowAtop]);
         const int va = atop / EPV - cv0;
         const int ka = (va >= 0 && va < clen) ? va / kThreads : -1;
 #pragma unroll
