@@ -19,6 +19,8 @@ from ._binding import (  # noqa: F401
     OPD_FLAG_NEG_L,
     OPD_FLAG_SPIN_TIMEOUT,
     OpdError,
+    check_mode,
+    debug_reserve_flags,
     length_head_loss,
     lmhead_fused_fwd_bwd_verify,
     library_path,
@@ -28,6 +30,7 @@ from ._binding import (  # noqa: F401
     opd_loss_fwd,
     pack_first_fit,
     read_flags,
+    set_check,
     set_spin_limit,
     stream_probe,
     verify_accept_len,

@@ -13,6 +13,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <unordered_map>
 
 #include "opd_internal.h"
 
@@ -25,7 +26,19 @@ namespace {
 
 thread_local std::string g_last_error;
 std::atomic<uint32_t> g_spin_limit{0};
-std::atomic<uint32_t> g_flag_next{0};  // host-chosen exchange flags: offsets into [2^31, 2^32)
+
+// Host-chosen exchange flags: offsets into [2^31, 2^32). When the range is used up it restarts at
+// its bottom and the generation count goes up; a workspace last used in an earlier generation may
+// hold units whose flags the new range hands out again, so its units are zeroed before its next
+// launch. Workspaces are tracked by address.
+std::mutex g_flag_mu;
+uint32_t g_flag_next = 0;
+uint64_t g_flag_gen = 0;
+std::unordered_map<const void*, uint64_t> g_ws_gen;
+
+// Check mode (OPD_CHECK=1 in the environment, or opd_set_check): every call synchronises its stream,
+// reads the workspace's sticky flag word and returns OPD_ERR_DEVICE if a bit is set.
+std::atomic<int> g_check{-1};
 
 constexpr int64_t kMaxVocab = 1 << 19;  // 524,288 logits per row
 
@@ -167,14 +180,41 @@ opd_status_t plan(int mode, int in_bf16, int out_bf16, int dev_flags, int64_t n_
 
 // Exchange flags for an eager launch: a fresh range in [2^31 + 1, 2^32), disjoint from the device
 // epoch's range [1, 2^31) that captured launches use, so the two kinds never take each other's
-// units for their own.
-uint32_t reserve_host_flags(uint32_t count) {
-  while (true) {
-    const uint32_t off = g_flag_next.fetch_add(count);
-    if ((uint64_t)off + count < 0x80000000ull) return 0x80000000u + off;
-    uint32_t expected = off + count;  // wrap: restart the offsets (the first caller past the end does)
-    g_flag_next.compare_exchange_strong(expected, 0u);
+// units for their own. Returns the base (first flag minus 1); *must_clear is set when the workspace
+// was last used before the range restarted (its units must be zeroed before this launch).
+uint32_t reserve_host_flags(const void* ws, uint32_t count, bool* must_clear) {
+  std::lock_guard<std::mutex> lk(g_flag_mu);
+  if ((uint64_t)g_flag_next + count >= 0x80000000ull) {
+    g_flag_next = 0;
+    ++g_flag_gen;
   }
+  const uint32_t base = 0x80000000u + g_flag_next;
+  g_flag_next += count;
+  auto it = g_ws_gen.find(ws);
+  *must_clear = it != g_ws_gen.end() && it->second != g_flag_gen;
+  g_ws_gen[ws] = g_flag_gen;  // a workspace seen for the first time is zero-filled by contract
+  return base;
+}
+
+bool check_mode() {
+  int v = g_check.load();
+  if (v < 0) {
+    const char* e = std::getenv("OPD_CHECK");
+    v = (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+    int expected = -1;
+    g_check.compare_exchange_strong(expected, v);
+    v = g_check.load();
+  }
+  return v != 0;
+}
+
+std::string flag_text(uint32_t f) {
+  std::string t;
+  if (f & OPD_FLAG_NEG_L) t += " negative L;";
+  if (f & OPD_FLAG_BAD_OFFSETS) t += " malformed offsets;";
+  if (f & OPD_FLAG_SPIN_TIMEOUT) t += " cross-workgroup wait timed out (outputs invalid);";
+  if (f & OPD_FLAG_BAD_TOKEN) t += " proposal outside the vocabulary;";
+  return t;
 }
 
 // True unless the stream is known not to be capturing: a captured launch takes its flags from the
@@ -230,9 +270,16 @@ opd_status_t run_team(int mode, const void* z, const void* y, opd_dtype_t dt, in
   const int64_t iters = (n_rows + g.n_teams - 1) / g.n_teams;
   if (2 * iters + 2 > 0x3fffffff) return fail(OPD_ERR_SHAPE, "too many rows");
   p.flag_count = (uint32_t)(2 * iters + 2);
-  p.flag_base = dev_flags ? 0u : reserve_host_flags(p.flag_count);
+  bool clear = false;
+  p.flag_base = dev_flags ? 0u : reserve_host_flags(ws, p.flag_count, &clear);
   p.spin_limit = spin_limit();
-  hipError_t e = opd::launch_team(p, mode, in_bf16, out_bf16, g.K, g.grid, stream);
+  hipError_t e = hipSuccess;
+  if (clear) {  // the host range restarted since this workspace was last used: zero its units
+    e = opd::launch_fill_u32(reinterpret_cast<uint32_t*>(p.units), 0u,
+                             (opd::kWorkspaceBytes - opd::kHeaderBytes) / sizeof(uint32_t), stream);
+    if (e != hipSuccess) return hip_fail(e, "clearing the exchange units");
+  }
+  e = opd::launch_team(p, mode, in_bf16, out_bf16, g.K, g.grid, stream);
   if (e != hipSuccess) return hip_fail(e, "team kernel launch");
   return OPD_OK;
 }
@@ -254,6 +301,25 @@ opd_status_t run_accept(const opd_blocks_t* blocks, int64_t n_rows, const int32_
   return OPD_OK;
 }
 
+// Check mode: once a call's work is enqueued, synchronise the stream, read the sticky flag word and
+// report a set bit as OPD_ERR_DEVICE (the word is then cleared). Skipped for a stream that is being
+// captured (it cannot be synchronised); launch errors surfaced by the synchronisation are OPD_ERR_HIP.
+opd_status_t finish(opd_status_t s, void* ws, hipStream_t stream) {
+  if (s != OPD_OK || !ws || !check_mode()) return s;
+  if (stream_may_be_captured(stream)) return s;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "check mode: reading the device flags");
+  if (v == 0) return OPD_OK;
+  e = opd::launch_fill_u32(static_cast<uint32_t*>(ws), 0u, 1, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "check mode: clearing the device flags");
+  char head[40];
+  std::snprintf(head, sizeof(head), "device flags 0x%x:", v);
+  return fail(OPD_ERR_DEVICE, std::string(head) + flag_text(v));
+}
+
 }  // namespace
 
 namespace opd {
@@ -264,7 +330,7 @@ extern "C" {
 
 size_t opd_workspace_size(void) { return opd::kWorkspaceBytes; }
 
-opd_status_t opd_loss_fwd(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab, int64_t ld,
+static opd_status_t opd_loss_fwd_impl(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab, int64_t ld,
                           float alpha, float tau, float* loss, int32_t* target_top1, int32_t* draft_top1,
                           float* row_stats, void* ws, size_t ws_bytes, hipStream_t stream) {
   opd_status_t s = check_logits(z, y, dt, n_rows, vocab, ld);
@@ -277,7 +343,7 @@ opd_status_t opd_loss_fwd(const void* z, const void* y, opd_dtype_t dt, int64_t 
                   row_stats, nullptr, OPD_F32, vocab, ws, stream);
 }
 
-opd_status_t opd_loss_bwd(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab, int64_t ld,
+static opd_status_t opd_loss_bwd_impl(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab, int64_t ld,
                           float alpha, float tau, const float* row_stats, const int32_t* target_top1,
                           const float* grad_loss, void* dz, opd_dtype_t dz_dt, int64_t ld_dz, void* ws,
                           size_t ws_bytes, hipStream_t stream) {
@@ -325,7 +391,7 @@ opd_status_t opd_loss_bwd(const void* z, const void* y, opd_dtype_t dt, int64_t 
   return OPD_OK;
 }
 
-opd_status_t verify_accept_len(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+static opd_status_t verify_accept_len_impl(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
                                int64_t ld, const opd_blocks_t* blocks, int32_t* target_top1, int32_t* draft_top1,
                                int32_t* accept_len, void* ws, size_t ws_bytes, hipStream_t stream) {
   opd_status_t s = check_logits(z, y, dt, n_rows, vocab, ld);
@@ -340,7 +406,7 @@ opd_status_t verify_accept_len(const void* z, const void* y, opd_dtype_t dt, int
   return run_accept(blocks, n_rows, draft_top1, target_top1, accept_len, ws, stream);
 }
 
-opd_status_t opd_fused_fwd_bwd_verify(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+static opd_status_t opd_fused_fwd_bwd_verify_impl(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
                                       int64_t ld, const opd_blocks_t* blocks, float alpha, float tau,
                                       const float* grad_loss, float* loss, int32_t* target_top1, int32_t* draft_top1,
                                       float* row_stats, void* dz, opd_dtype_t dz_dt, int64_t ld_dz,
@@ -361,7 +427,7 @@ opd_status_t opd_fused_fwd_bwd_verify(const void* z, const void* y, opd_dtype_t 
   return run_accept(blocks, n_rows, draft_top1, target_top1, accept_len, ws, stream);
 }
 
-opd_status_t opd_length_head_loss(const int32_t* target_top1, const int32_t* draft_top1, int64_t n_rows,
+static opd_status_t opd_length_head_loss_impl(const int32_t* target_top1, const int32_t* draft_top1, int64_t n_rows,
                                   const int32_t* offsets, int32_t n_blocks, const float* head_logit,
                                   const float* grad, int32_t* accept_full, float* label, float* loss,
                                   float* dlogit, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -391,7 +457,7 @@ opd_status_t opd_length_head_loss(const int32_t* target_top1, const int32_t* dra
   return OPD_OK;
 }
 
-opd_status_t opd_verify_sample(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+static opd_status_t opd_verify_sample_impl(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
                                int64_t ld, const opd_blocks_t* blocks, const int32_t* draft_tokens,
                                const float* u_accept, const float* u_resample, float temperature,
                                int32_t* accept_len, int32_t* out_token, float* row_lse, void* ws,
@@ -446,7 +512,7 @@ size_t opd_lmhead_scratch_size(int64_t chunk_rows, int64_t vocab, int64_t ld_y) 
   return (size_t)(zb + db);
 }
 
-opd_status_t opd_lmhead_fused_fwd_bwd_verify(const void* h, const void* W, int64_t hidden, const void* y,
+static opd_status_t opd_lmhead_fused_fwd_bwd_verify_impl(const void* h, const void* W, int64_t hidden, const void* y,
                                              opd_dtype_t dt_y, int64_t n_rows, int64_t vocab, int64_t ld_y,
                                              const opd_blocks_t* blocks, float alpha, float tau,
                                              const float* grad_loss, float* loss, int32_t* target_top1,
@@ -541,7 +607,97 @@ opd_status_t opd_stream_probe(const void* a, const void* b, void* c, size_t byte
   return OPD_OK;
 }
 
+// ---- public entry points: the work above, then the check-mode test of the device flags
+
+opd_status_t opd_loss_fwd(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab, int64_t ld,
+                          float alpha, float tau, float* loss, int32_t* target_top1, int32_t* draft_top1,
+                          float* row_stats, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return finish(opd_loss_fwd_impl(z, y, dt, n_rows, vocab, ld, alpha, tau, loss, target_top1, draft_top1, row_stats,
+                                  ws, ws_bytes, stream),
+                ws, stream);
+}
+
+opd_status_t opd_loss_bwd(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab, int64_t ld,
+                          float alpha, float tau, const float* row_stats, const int32_t* target_top1,
+                          const float* grad_loss, void* dz, opd_dtype_t dz_dt, int64_t ld_dz, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  return finish(opd_loss_bwd_impl(z, y, dt, n_rows, vocab, ld, alpha, tau, row_stats, target_top1, grad_loss, dz,
+                                  dz_dt, ld_dz, ws, ws_bytes, stream),
+                ws, stream);
+}
+
+opd_status_t verify_accept_len(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+                               int64_t ld, const opd_blocks_t* blocks, int32_t* target_top1, int32_t* draft_top1,
+                               int32_t* accept_len, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return finish(verify_accept_len_impl(z, y, dt, n_rows, vocab, ld, blocks, target_top1, draft_top1, accept_len, ws,
+                                       ws_bytes, stream),
+                ws, stream);
+}
+
+opd_status_t opd_fused_fwd_bwd_verify(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+                                      int64_t ld, const opd_blocks_t* blocks, float alpha, float tau,
+                                      const float* grad_loss, float* loss, int32_t* target_top1, int32_t* draft_top1,
+                                      float* row_stats, void* dz, opd_dtype_t dz_dt, int64_t ld_dz,
+                                      int32_t* accept_len, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return finish(opd_fused_fwd_bwd_verify_impl(z, y, dt, n_rows, vocab, ld, blocks, alpha, tau, grad_loss, loss,
+                                              target_top1, draft_top1, row_stats, dz, dz_dt, ld_dz, accept_len, ws,
+                                              ws_bytes, stream),
+                ws, stream);
+}
+
+opd_status_t opd_length_head_loss(const int32_t* target_top1, const int32_t* draft_top1, int64_t n_rows,
+                                  const int32_t* offsets, int32_t n_blocks, const float* head_logit,
+                                  const float* grad, int32_t* accept_full, float* label, float* loss,
+                                  float* dlogit, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return finish(opd_length_head_loss_impl(target_top1, draft_top1, n_rows, offsets, n_blocks, head_logit, grad,
+                                          accept_full, label, loss, dlogit, ws, ws_bytes, stream),
+                ws, stream);
+}
+
+opd_status_t opd_verify_sample(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows, int64_t vocab,
+                               int64_t ld, const opd_blocks_t* blocks, const int32_t* draft_tokens,
+                               const float* u_accept, const float* u_resample, float temperature,
+                               int32_t* accept_len, int32_t* out_token, float* row_lse, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  return finish(opd_verify_sample_impl(z, y, dt, n_rows, vocab, ld, blocks, draft_tokens, u_accept, u_resample,
+                                       temperature, accept_len, out_token, row_lse, ws, ws_bytes, stream),
+                ws, stream);
+}
+
+opd_status_t opd_lmhead_fused_fwd_bwd_verify(const void* h, const void* W, int64_t hidden, const void* y,
+                                             opd_dtype_t dt_y, int64_t n_rows, int64_t vocab, int64_t ld_y,
+                                             const opd_blocks_t* blocks, float alpha, float tau,
+                                             const float* grad_loss, float* loss, int32_t* target_top1,
+                                             int32_t* draft_top1, float* row_stats, float* dh, float* dW,
+                                             int32_t* accept_len, void* scratch, size_t scratch_bytes,
+                                             int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return finish(opd_lmhead_fused_fwd_bwd_verify_impl(h, W, hidden, y, dt_y, n_rows, vocab, ld_y, blocks, alpha, tau,
+                                                     grad_loss, loss, target_top1, draft_top1, row_stats, dh, dW,
+                                                     accept_len, scratch, scratch_bytes, chunk_rows, ws, ws_bytes,
+                                                     stream),
+                ws, stream);
+}
+
 void opd_set_spin_limit(uint32_t spins) { g_spin_limit.store(spins); }
+
+void opd_set_check(int on) { g_check.store(on ? 1 : 0); }
+
+int opd_get_check(void) { return check_mode() ? 1 : 0; }
+
+opd_status_t opd_debug_reserve_flags(const void* ws, uint32_t count, int64_t next_offset, uint32_t* base,
+                                     int* must_clear) {
+  if (!base || !must_clear) return fail(OPD_ERR_NULL, "base and must_clear must be non-NULL");
+  if (count == 0 || count > 0x3fffffffu) return fail(OPD_ERR_SHAPE, "count must be in [1, 2^30)");
+  if (next_offset >= 0x80000000ll) return fail(OPD_ERR_SHAPE, "next_offset must be below 2^31");
+  if (next_offset >= 0) {
+    std::lock_guard<std::mutex> lk(g_flag_mu);
+    g_flag_next = (uint32_t)next_offset;
+  }
+  bool clear = false;
+  *base = reserve_host_flags(ws, count, &clear);
+  *must_clear = clear ? 1 : 0;
+  return OPD_OK;
+}
 
 const char* opd_status_string(opd_status_t s) {
   switch (s) {
@@ -553,6 +709,7 @@ const char* opd_status_string(opd_status_t s) {
     case OPD_ERR_PARAM: return "OPD_ERR_PARAM: alpha or tau invalid";
     case OPD_ERR_WORKSPACE: return "OPD_ERR_WORKSPACE: workspace missing or too small";
     case OPD_ERR_HIP: return "OPD_ERR_HIP: HIP runtime error";
+    case OPD_ERR_DEVICE: return "OPD_ERR_DEVICE: the call raised device flags (check mode)";
   }
   return "unknown status";
 }

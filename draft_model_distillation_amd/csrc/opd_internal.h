@@ -16,12 +16,18 @@ constexpr int kStage1Units = 7;
 constexpr int kStage2Units = 5;  // S, clipped sum, lowest indices of the row maxima of z and y, z at the latter
 constexpr int kMaxGrid = 4096;  // upper bound on co-resident workgroups the workspace is sized for
 // Workspace layout: [0, 256) header, then the exchange units. The header holds the sticky flag word
-// (byte 0), the exchange-flag epoch (byte 64) and the count of row-team workgroups that finished the
-// current launch (byte 128), each on its own cache line. A zero-filled header is the initial state.
+// (byte 0), the exchange-flag epoch (byte 64), the count of row-team workgroups that finished the
+// current launch (byte 128) and the 64-bit arrival ticket counter (byte 192), each on its own cache
+// line. A zero-filled header is the initial state.
 constexpr size_t kHeaderBytes = 256;
-constexpr int kEpochWord = 16;  // uint32 index of the epoch in the header
-constexpr int kDoneWord = 32;   // uint32 index of the finished-workgroup count
-constexpr size_t kUnitBytesPerWg = 2 * 8 * 8;  // two stages x up to 8 units x 8 bytes
+constexpr int kEpochWord = 16;   // uint32 index of the epoch in the header
+constexpr int kDoneWord = 32;    // uint32 index of the finished-workgroup count
+constexpr int kArriveQword = 24; // uint64 index of the arrival ticket counter
+// Three stages per team: exchange 1 alternates between stages 0 and 1 by row-iteration parity (a
+// member that moves on to its next row must not overwrite a value a slower member of the team has yet
+// to read), exchange 2 uses stage 2.
+constexpr int kStages = 3;
+constexpr size_t kUnitBytesPerWg = kStages * 8 * 8;  // three stages x up to 8 units x 8 bytes
 constexpr size_t kWorkspaceBytes = kHeaderBytes + (size_t)kMaxGrid * kUnitBytesPerWg;
 
 // Sticky device flag bits (same values as the public OPD_FLAG_* macros).
@@ -30,6 +36,9 @@ constexpr uint32_t kFlagBadOffsets = 2u;
 constexpr uint32_t kFlagSpinTimeout = 4u;
 constexpr uint32_t kFlagBadToken = 8u;
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
+// A device epoch past this value is restarted at 0 by the last workgroup of a launch, which first
+// zeroes every exchange unit (no flag of the range that ends can then match a stale unit).
+constexpr uint32_t kEpochRestart = 0x40000000u;
 constexpr int kMaxTeamSize = 128;
 
 enum Mode : int { kFused = 0, kForward = 1, kTop1 = 2 };
@@ -54,7 +63,7 @@ struct TeamParams {
   float* row_stats;     // [n_rows][8]; nullable in kTop1 mode
   uint8_t* dz;
   int64_t ld_dz_bytes;
-  uint64_t* units;  // exchange units [n_teams][2][G][8]
+  uint64_t* units;  // exchange units [n_teams][kStages][G][8]
   uint32_t* flags;  // workspace header: sticky flag word, epoch (kEpochWord), done count (kDoneWord)
   uint32_t flag_count;  // exchange flags this launch uses (2 per row iteration + 2)
   uint32_t flag_base;   // first flag minus 1, chosen by the host (>= 2^31); 0: from the workspace epoch

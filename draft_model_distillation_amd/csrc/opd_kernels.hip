@@ -290,6 +290,8 @@ struct Shared {
   float wza[4];      // z at the wave's argmax of y
   float row[12];     // row constants, written by wave 0
   int err;
+  int last;          // this workgroup is the last of the launch to finish (device-epoch launches)
+  int ticket;        // this workgroup's place in the launch's arrival order
   uint32_t fbase;    // first exchange flag of this launch
 };
 
@@ -529,17 +531,31 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
   __shared__ VecMax<EPV> vmlds[K * kThreads];  // per-vector maxima from phase A to phase B
   const int tid = thread_id();
   const int wave = tid >> 6;
-  const int b = block_id_x();
-  // consecutive workgroups form a team, so its members land on different XCDs (round-robin
-  // dispatch); keeping a team on one XCD measured slower
+  // Teams are formed in arrival order: each workgroup draws a ticket from a 64-bit counter in the
+  // workspace header when it starts, and tickets t .. t + G - 1 (mod the grid) form a team. A launch
+  // draws exactly one ticket per workgroup, so its tickets are consecutive integers and their
+  // residues modulo the grid size are a permutation of the workgroups, whatever value an earlier
+  // launch left in the counter. A team therefore consists of workgroups that are already running:
+  // if other work on the device delays part of the grid, the late workgroups form the later teams
+  // (at most one team is partly formed at a time), instead of leaving a member of every team
+  // unscheduled while the others wait for it. Arrival follows dispatch order, which spreads a team
+  // over the XCDs (round-robin dispatch); keeping a team on one XCD measured slower.
+  if (tid == 0) {
+    const uint64_t t = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(P.flags) + kArriveQword, (uint64_t)1,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.ticket = (int)(t % (uint64_t)(P.n_teams * P.G));
+  }
+  __syncthreads();
+  const int b = sh.ticket;
   const int team = b / P.G;
   const int chunk = b % P.G;
   const int G = P.G;
   const int cv0 = chunk * P.chunk_vec;
   const int clen0 = min(P.chunk_vec, P.nvec - cv0);  // vectors in this chunk (uniform)
   const bool tail_chunk = (cv0 + clen0 == P.nvec) && (P.nvec * EPV != P.vocab);
-  uint64_t* const units1 = P.units + (size_t)team * 2 * G * 8;
-  uint64_t* const units2 = units1 + (size_t)G * 8;
+  // this team's units: exchange 1 of even / odd row iterations in stages 0 / 1, exchange 2 in stage 2
+  uint64_t* const units_team = P.units + (size_t)team * kStages * G * 8;
+  uint64_t* const units2 = units_team + (size_t)2 * G * 8;
   // Exchange flags are base + 1 .. base + flag_count. An eager call gets its range from the host
   // (flag_base, flags >= 2^31). A call captured into a graph, whose kernel arguments are frozen for
   // every replay, runs the DevFlags instantiation, which takes the range from the epoch in the
@@ -766,6 +782,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     // ---- exchange 1: wave 0 publishes the chunk values, gathers the members' values and forms the
     // row constants; the other waves wait at the barrier
     const uint32_t flag1 = sh.fbase + 2u * (uint32_t)iter;
+    // Exchange 1 alternates between two stages by row parity. In the forward and top-1 modes a member
+    // may finish its row (and publish the next row's exchange 1) before a slower member has gathered
+    // this row's values: with one stage it would overwrite them. Two rows later the slot is free
+    // again, because this member's gather of the row in between waited for every member to publish
+    // it, which each does only after finishing this row.
+    uint64_t* const units1 = units_team + (size_t)(iter & 1) * G * 8;
     // values per member in exchange 1: maxima and sums (the top-1 indices follow in exchange 2), or
     // in top-1 mode the maxima and their lowest indices
     constexpr int NU1 = kSums ? 4 : kStage1Units;
@@ -1084,12 +1106,29 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     // then every workgroup of this launch has read it. Relaxed agent-scope atomics; the kernel
     // boundary orders them before the next launch's read.
     if constexpr (DevFlags) {
+      // this wave published every exchange value of the workgroup: wait until those stores are
+      // done before counting the workgroup as finished (the last one may zero the units below)
+      __builtin_amdgcn_s_waitcnt(0);
       const uint32_t grid = (uint32_t)(P.n_teams * P.G);
       const uint32_t done = __hip_atomic_fetch_add(P.flags + kDoneWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (done + 1u == grid) {
+      sh.last = done + 1u == grid;
+    }
+  }
+  if constexpr (DevFlags) {
+    __syncthreads();
+    if (sh.last) {
+      uint32_t next = (sh.fbase - 1u) + P.flag_count;
+      if (next > kEpochRestart) {
+        // The range restarts: zero every exchange unit first, so that no unit written in the range
+        // that ends can carry a flag of the next one. No other workgroup of this launch is left.
+        constexpr size_t n_units = (kWorkspaceBytes - kHeaderBytes) / 8;
+        for (size_t i = tid; i < n_units; i += kThreads)
+          __hip_atomic_store(P.units + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        next = 0;
+      }
+      if (tid == 0) {
         __hip_atomic_store(P.flags + kDoneWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(P.flags + kEpochWord, (sh.fbase - 1u) + P.flag_count, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(P.flags + kEpochWord, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }

@@ -44,7 +44,11 @@
  *     may be replayed any number of times; other calls take it from the host.
  *   - Device-side content problems (negative L, malformed offsets, a cross-workgroup wait that
  *     exceeded its bound) set bits in a sticky flag word inside the workspace, read with
- *     opd_read_flags().
+ *     opd_read_flags(), or reported by the call itself in check mode (opd_set_check, OPD_CHECK=1).
+ *   - The row-team kernels keep all G workgroups of a row resident at once and exchange partial
+ *     results between them with bounded waits. The grid is sized for an otherwise idle device; if
+ *     other work keeps a member of a team from being scheduled, the waits end on their bound and
+ *     the call raises OPD_FLAG_SPIN_TIMEOUT (outputs invalid) instead of hanging.
  */
 #ifndef OPD_MI355X_H
 #define OPD_MI355X_H
@@ -68,7 +72,8 @@ typedef enum {
   OPD_ERR_ALIGN = 4,      /* base pointer or row pitch not a multiple of 16 bytes              */
   OPD_ERR_PARAM = 5,      /* alpha outside [0, 1] or NaN, tau NaN                              */
   OPD_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than opd_workspace_size()              */
-  OPD_ERR_HIP = 7         /* a HIP call failed; opd_last_error() has the HIP error text       */
+  OPD_ERR_HIP = 7,        /* a HIP call failed; opd_last_error() has the HIP error text       */
+  OPD_ERR_DEVICE = 8      /* check mode only: the call raised device flags (see opd_set_check) */
 } opd_status_t;
 
 /* Bits of the sticky device flag word (see opd_read_flags). */
@@ -296,6 +301,28 @@ opd_status_t opd_stream_probe(const void* a, const void* b, void* c, size_t byte
 /* Debug knob for tests of the failure path: caps every cross-workgroup wait at `spins` polls
  * (0 restores the default bound). Affects launches made after the call, process-wide. */
 void opd_set_spin_limit(uint32_t spins);
+
+/* Check mode, for debugging and for callers that need failures surfaced at once. When on, every
+ * call that takes a workspace synchronises its stream after enqueuing its work, reads the sticky
+ * flag word, and if a bit is set clears it and returns OPD_ERR_DEVICE (opd_last_error() names the
+ * flags); a kernel failure found by the synchronisation returns OPD_ERR_HIP. Calls made while their
+ * stream is being captured into a graph are not checked (they cannot synchronise). Off by default;
+ * the environment variable OPD_CHECK=1 turns it on at the first call, opd_set_check(0 / 1) at any
+ * time (process-wide). opd_get_check() returns the current setting. */
+void opd_set_check(int on);
+int opd_get_check(void);
+
+/* Exchange-flag bookkeeping of calls made outside stream capture, exposed so that the restart of the
+ * flag range can be tested without a GPU. Each launch takes `count` fresh flags from a process-wide
+ * range of 2^31; when the range is used up it restarts, and a workspace last used before the
+ * restart has its exchange units zeroed (a fill kernel on the call's stream) before its next
+ * launch, so that no unit left from the previous range can match a flag handed out again.
+ * This function performs the reservation for workspace `ws` (only its address is used) without
+ * launching anything: *base = first flag - 1, *must_clear = whether a launch would zero the units
+ * first. next_offset >= 0 first moves the range's counter to that offset (tests); -1 leaves it.
+ * Errors: OPD_ERR_NULL, OPD_ERR_SHAPE (count 0 or >= 2^30, next_offset >= 2^31). */
+opd_status_t opd_debug_reserve_flags(const void* ws, uint32_t count, int64_t next_offset, uint32_t* base,
+                                     int* must_clear);
 
 /* Static description of a status code, and the detail text of the last error on this thread. */
 const char* opd_status_string(opd_status_t s);

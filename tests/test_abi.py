@@ -38,7 +38,7 @@ def test_header_declarations_are_all_exported(lib):
 
 def test_workspace_size_and_status_strings(lib):
     assert lib.opd_workspace_size() > 0
-    for s in range(8):
+    for s in range(9):
         assert lib.opd_status_string(s).decode().startswith("OPD_")
 
 
