@@ -18,8 +18,14 @@ HBM. Prints one JSON line:
   the same buffers (the ceilings of the two halves of the pattern). traffic = HBM bytes per launch from the rocprofv3
   FETCH_SIZE / WRITE_SIZE counters recorded in profiles/ for the current kernel source (null if the
   kernel changed since they were taken).
-* cpu_baseline: the float64 oracle (loss, gradient, top-1s, accept lengths) on a bounded sample of
-  the same workload, on the host cores, timed on rank 0 before the GPU is touched.
+* cpu_baseline: the float64 oracle (loss, gradient, top-1s, accept lengths) on every row of the
+  same workload (--cpu-blocks limits it), one process per host core this process may use (at most
+  16), timed before the GPU is touched; the affinity count, os.cpu_count() and the CPU model are
+  reported beside it.
+* extras.per_config: the fused call timed one call at a time with HIP events on each workload (the
+  16-row decode rotating over copies that together exceed the 256 MB Infinity Cache, the 2048-row
+  serving batch, the packed ragged batch and the step's own workload): median, p10 and p90 per call,
+  rows/s and algorithmic GB/s at the median.
 """
 
 from __future__ import annotations
@@ -88,26 +94,43 @@ _SAMPLE = {}
 def _oracle_rows(idx_range):
     from oracle import opd_oracle as O
 
-    z, y, alpha, tau = _SAMPLE["z"], _SAMPLE["y"], _SAMPLE["alpha"], _SAMPLE["tau"]
+    wl, alpha, tau = _SAMPLE["wl"], _SAMPLE["alpha"], _SAMPLE["tau"]
     out = []
     for i in range(*idx_range):
-        dz, info = O.row_grad(z[i], y[i], alpha, tau)
+        z, y = wl.rows_f64([i])  # exact values of the stored row (bf16 -> float64)
+        dz, info = O.row_grad(z[0], y[0], alpha, tau)
         out.append((info["loss"], info["target_top1"], info["draft_top1"]))
     return out
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, n_blocks_sample: int):
-    """Oracle on the first n_blocks_sample blocks of the workload; returns the cpu_baseline dict."""
+    """Oracle on the first n_blocks_sample blocks (all by default) of the workload, one worker process
+    per host core this process may use (at most 16, the host share of one GPU); returns the
+    cpu_baseline dict."""
     import multiprocessing as mp
 
     from oracle import opd_oracle as O
 
-    nb = min(n_blocks_sample, len(wl.lengths))
+    nb = min(n_blocks_sample, len(wl.lengths)) if n_blocks_sample > 0 else len(wl.lengths)
     rows = int(wl.offsets[nb])
-    z, y = wl.rows_f64(range(rows))
-    _SAMPLE.update(z=z, y=y, alpha=wl.recipe.alpha, tau=wl.recipe.tau)
+    _SAMPLE.update(wl=wl, alpha=wl.recipe.alpha, tau=wl.recipe.tau)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
     cores = synth.default_workers()
-    step = max(1, rows // (cores * 4))
+    step = max(1, rows // (cores * 8))
     chunks = [(r, min(rows, r + step)) for r in range(0, rows, step)]
     ctx = mp.get_context("fork")
     with ctx.Pool(cores) as pool:
@@ -123,8 +146,11 @@ def cpu_baseline(wl, n_blocks_sample: int):
         "unit": "rows/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"first {nb} blocks = {rows} rows of the workload (float64 loss, dz, top-1s, accept lengths), "
-                  f"{dt:.1f} s wall on {cores} host processes",
+        "sample": f"{'all' if nb == len(wl.lengths) else 'first'} {nb} blocks = {rows} rows of the workload "
+                  f"(float64 loss, dz, top-1s, accept lengths), {dt:.1f} s wall on {cores} host processes",
+        "affinity_cores": affinity,
+        "os_cpu_count": os.cpu_count(),
+        "cpu_model": _cpu_model(),
     }
 
 
@@ -141,13 +167,73 @@ def to_device(arr, dtype_name):
     return t.pin_memory().cuda(non_blocking=False) if arr.nbytes < (1 << 30) else t.cuda()
 
 
+def new_outputs(torch, n, vocab, n_blocks, dz_dtype, dev):
+    return {
+        "loss": torch.empty(n, dtype=torch.float32, device=dev),
+        "target_top1": torch.empty(n, dtype=torch.int32, device=dev),
+        "draft_top1": torch.empty(n, dtype=torch.int32, device=dev),
+        "row_stats": torch.empty(n, 8, dtype=torch.float32, device=dev),
+        "dz": torch.empty(n, vocab, dtype=dz_dtype, device=dev),
+        "accept_len": torch.empty(n_blocks, dtype=torch.int32, device=dev),
+    }
+
+
+def call_stats(opd, stream, sets, off, lens, rec, dz_dtype, ws, calls, warmup):
+    """Times `calls` fused calls one at a time (HIP events on the stream before and after each), the
+    i-th call on input set i mod len(sets); returns median / p10 / p90 and the rates at the median."""
+    import torch
+
+    def call(i):
+        zc, yc, oc = sets[i % len(sets)]
+        opd.opd_fused_fwd_bwd_verify(zc, yc, off, lens, rec.alpha, rec.tau, out=oc, ws=ws)
+
+    for i in range(warmup):
+        call(i)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+    torch.cuda.synchronize()
+    # The host needs longer to enqueue a small call than the GPU takes to run it. A spin kernel first
+    # holds the stream while every call is enqueued, so that each event pair brackets GPU time only.
+    t0 = time.perf_counter()
+    for i in range(min(calls, 20)):
+        call(i)
+    host_s = (time.perf_counter() - t0) / min(calls, 20)
+    torch.cuda.synchronize()
+    hold_s = 1.5 * host_s * calls + 0.01
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(1 << 20)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_s = (1 << 20) / max(e0.elapsed_time(e1) * 1e-3, 1e-9)
+    torch.cuda._sleep(int(min(hold_s, 5.0) * cycles_per_s))
+    for i in range(calls):
+        starts[i].record(stream)
+        call(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    n = sets[0][0].shape[0]
+    in_b = 2 if rec.dtype == "bf16" else 4
+    out_b = 2 if dz_dtype == torch.bfloat16 else 4
+    alg = n * (rec.vocab * (2 * in_b + out_b) + ROW_OUTPUT_BYTES)
+    med = float(np.median(ms))
+    return {"rows": int(n), "calls": int(calls), "median_us": med * 1e3,
+            "p10_us": float(np.percentile(ms, 10)) * 1e3, "p90_us": float(np.percentile(ms, 90)) * 1e3,
+            "rows_per_s": n / (med * 1e-3), "alg_gbs": alg / (med * 1e-3) / 1e9,
+            "frac_of_peak": alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="train", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--cpu-blocks", type=int, default=512, help="blocks of the workload timed on the oracle")
+    ap.add_argument("--cpu-blocks", type=int, default=0, help="blocks of the workload timed on the oracle (0: all)")
+    ap.add_argument("--no-extras", dest="extras", action="store_false",
+                    help="skip the per-call timing of the other workloads (16-row decode, 2048-row serving, "
+                         "packed batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lmhead", dest="lmhead", action="store_false",
                     help="skip timing the lm_head-fused path beside the step")
@@ -172,6 +258,14 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_blocks)
         print(f"[bench] cpu baseline: {cpu['value']:.1f} rows/s on {cpu['cores']} cores", file=sys.stderr, flush=True)
+
+    # the other workloads, timed per call beside the step (generated before the GPU is touched)
+    extra_wls = {}
+    if args.extras and not args.profile:
+        for name in ("decode1", "conc128", "packed"):
+            if name != args.workload:
+                extra_wls[name] = synth.make(name)
+        print(f"[bench] generated {sorted(extra_wls)}", file=sys.stderr, flush=True)
 
     import torch
 
@@ -227,6 +321,13 @@ def main():
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
     if opd.read_flags(ws, clear=True) != 0:
         print("[bench] device flags raised during the timed region", file=sys.stderr)
+        sys.exit(1)
+
+    # per-call times of the step (HIP events around each call on its stream): median, p10, p90
+    per_config = {args.workload: call_stats(opd, stream, [(z, y, out)], off, lens, rec, dz_dtype, ws,
+                                            max(args.steps, 20), args.warmup)}
+    if opd.read_flags(ws, clear=True) != 0:
+        print("[bench] device flags raised during the per-call timing", file=sys.stderr)
         sys.exit(1)
 
     # achievable bandwidth of the same traffic pattern (read z and y, write a dz-sized buffer) with
@@ -356,6 +457,33 @@ def main():
             sys.exit(1)
         del hh, Wm, y32, lout
 
+    # the other workloads: per-call times of the fused call on each, with its own inputs. The 16-row
+    # decode's working set (14.6 MB) would sit in the caches if one copy were called repeatedly, so
+    # its calls rotate over enough copies (at different addresses) to exceed the 256 MB Infinity Cache.
+    for name, wlx in extra_wls.items():
+        rx = wlx.recipe
+        zx = to_device(wlx.z, rx.dtype)[:, : rx.vocab]
+        yx = to_device(wlx.y, rx.dtype)[:, : rx.vocab]
+        offx = torch.from_numpy(wlx.offsets).to(dev)
+        lensx = torch.from_numpy(wlx.lengths).to(dev)
+        dzx = torch.bfloat16 if rx.dz_dtype == "bf16" else torch.float32
+        per_copy = 3 * wlx.n_rows * rx.vocab * 2
+        copies = max(1, min(64, -(-(600 << 20) // per_copy))) if per_copy < (256 << 20) else 1
+        sets = []
+        for c in range(copies):
+            zc = zx if c == 0 else zx.clone()
+            yc = yx if c == 0 else yx.clone()
+            sets.append((zc, yc, new_outputs(torch, wlx.n_rows, rx.vocab, len(wlx.lengths), dzx, dev)))
+        calls = {"decode1": 2000, "conc128": 200, "packed": 200}.get(name, 50)
+        per_config[name] = call_stats(opd, stream, sets, offx, lensx, rx, dzx, ws, calls, 3)
+        per_config[name]["rotated_copies"] = copies
+        if opd.read_flags(ws, clear=True) != 0:
+            print(f"[bench] device flags raised on {name}", file=sys.stderr)
+            sys.exit(1)
+        del sets, zx, yx
+        torch.cuda.empty_cache()
+    del extra_wls
+
     # host packer: first fit of the workload's requests (their lengths, in order) under a budget
     # of half the workload's rows, per call through the binding
     lengths_np = np.diff(off.cpu().numpy())
@@ -432,6 +560,9 @@ def main():
                    # opd_lmhead_fused_fwd_bwd_verify per call (three bf16 GEMMs through rocBLAS + the
                    # row kernel); gemm_tflops counts the GEMM flops only, against 2.5 PFLOP/s dense bf16
                    "lmhead_fused": lmhead,
+                   # per workload: the fused call timed one call at a time with HIP events (median, p10,
+                   # p90 over the calls), rows/s and algorithmic GB/s at the median
+                   "per_config": per_config,
                    "packer_requests": int(lengths_np.size)},
     }
     print(json.dumps(result), flush=True)

@@ -157,11 +157,12 @@ def _dtype_code(t) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
 
 
-def _matrix(t, name: str):
+def _matrix(t, name: str, whole_vectors: bool = True):
     """(pointer, rows, cols, ld) of a row-major 2-D tensor whose rows may be padded.
 
-    The kernels may read a row up to its pitch, so the tensor's storage must hold rows * ld
-    elements from its first element on (true of row slices of a padded buffer)."""
+    The kernels read inputs in whole 16-byte vectors, so the storage of an input must reach the end
+    of the last row's last vector (true of row slices of a padded buffer); outputs are written up to
+    the last element only (whole_vectors=False)."""
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D [rows, vocab]")
     if t.shape[1] > 1 and t.stride(1) != 1:
@@ -170,8 +171,8 @@ def _matrix(t, name: str):
     if ld < t.shape[1]:
         raise ValueError(f"{name}: row pitch {ld} is shorter than a row ({t.shape[1]})")
     if t.shape[0] > 0 and t.shape[1] > 0 and t.device.type != "meta":
-        per = max(1, 16 // t.element_size())
-        last = ((t.shape[1] + per - 1) // per) * per  # the kernels read whole 16-byte vectors
+        per = max(1, 16 // t.element_size()) if whole_vectors else 1
+        last = ((t.shape[1] + per - 1) // per) * per
         span = (t.storage_offset() + (t.shape[0] - 1) * ld + last) * t.element_size()
         if span > t.untyped_storage().nbytes():
             raise ValueError(f"{name}: the storage ends before the last row's last 16-byte vector")
@@ -480,7 +481,7 @@ def opd_loss_bwd(z, y, alpha: float, tau: float, row_stats, target_top1, grad_lo
     _vector(grad_loss, "grad_loss", rows, torch.float32, optional=True)
     if dz is not None:
         _dtype_code(dz)
-        _, rows_d, vocab_d, _ = _matrix(dz, "dz")
+        _, rows_d, vocab_d, _ = _matrix(dz, "dz", whole_vectors=False)
         _require((rows_d, vocab_d) == (rows, vocab), f"dz must be [{rows}, {vocab}], got {tuple(dz.shape)}")
         _no_overlap(dz, z, "dz", "z")
         _no_overlap(dz, y, "dz", "y")
@@ -491,7 +492,7 @@ def opd_loss_bwd(z, y, alpha: float, tau: float, row_stats, target_top1, grad_lo
     ws = _workspace_arg(ws, dev)
     if dz is None:
         dz = _empty_rows(rows, vocab, dz_dtype or z.dtype, dev)
-    dzp, _, _, ld_dz = _matrix(dz, "dz")
+    dzp, _, _, ld_dz = _matrix(dz, "dz", whole_vectors=False)
     st = lib.opd_loss_bwd(zp, yp, dt, rows, vocab, ld, float(alpha), float(tau), row_stats.data_ptr(),
                           target_top1.data_ptr(), _ptr(grad_loss), dzp, _dtype_code(dz), ld_dz, ws.data_ptr(),
                           ws.numel(), _stream(dev))
@@ -629,7 +630,7 @@ def opd_fused_fwd_bwd_verify(z, y, offsets, lengths, alpha: float, tau: float, g
         _row_outputs(o, rows, n_blocks, ("loss", "target_top1", "draft_top1", "row_stats", "accept_len"))
         _require(o.get("dz") is not None, "out['dz'] is missing")
         _dtype_code(o["dz"])
-        _, rows_d, vocab_d, _ = _matrix(o["dz"], "dz")
+        _, rows_d, vocab_d, _ = _matrix(o["dz"], "dz", whole_vectors=False)
         _require((rows_d, vocab_d) == (rows, vocab), f"dz must be [{rows}, {vocab}], got {tuple(o['dz'].shape)}")
         _no_overlap(o["dz"], z, "dz", "z")
         _no_overlap(o["dz"], y, "dz", "y")
@@ -646,7 +647,7 @@ def opd_fused_fwd_bwd_verify(z, y, offsets, lengths, alpha: float, tau: float, g
         o["dz"] = _empty_rows(rows, vocab, dz_dtype or z.dtype, dev)
         o["accept_len"] = torch.empty(n_blocks, dtype=torch.int32, device=dev)
     _require(n_blocks == 0 or o.get("draft_top1") is not None, "draft_top1 is needed for verification")
-    dzp, _, _, ld_dz = _matrix(o["dz"], "dz")
+    dzp, _, _, ld_dz = _matrix(o["dz"], "dz", whole_vectors=False)
     st = lib.opd_fused_fwd_bwd_verify(
         zp, yp, dt, rows, vocab, ld, ctypes.byref(blocks) if blocks is not None else None,
         float(alpha), float(tau), _ptr(grad_loss), o["loss"].data_ptr(), o["target_top1"].data_ptr(),
@@ -654,3 +655,4 @@ def opd_fused_fwd_bwd_verify(z, y, offsets, lengths, alpha: float, tau: float, g
         o["accept_len"].data_ptr() if n_blocks else None, ws.data_ptr(), ws.numel(), _stream(dev))
     _check("opd_fused_fwd_bwd_verify", st)
     return o
+

@@ -267,6 +267,8 @@ opd_status_t run_team(int mode, const void* z, const void* y, opd_dtype_t dt, in
   p.ld_dz_bytes = ld_dz * (int64_t)dtype_size(dz_dt);
   p.units = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ws) + opd::kHeaderBytes);
   p.flags = static_cast<uint32_t*>(ws);
+  if ((size_t)g.grid * opd::kUnitBytesPerWg > opd::kWorkspaceBytes - opd::kHeaderBytes)
+    return fail(OPD_ERR_WORKSPACE, "launch needs more exchange units than the workspace holds");
   const int64_t iters = (n_rows + g.n_teams - 1) / g.n_teams;
   if (2 * iters + 2 > 0x3fffffff) return fail(OPD_ERR_SHAPE, "too many rows");
   p.flag_count = (uint32_t)(2 * iters + 2);

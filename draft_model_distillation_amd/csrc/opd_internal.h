@@ -16,13 +16,11 @@ constexpr int kStage1Units = 7;
 constexpr int kStage2Units = 5;  // S, clipped sum, lowest indices of the row maxima of z and y, z at the latter
 constexpr int kMaxGrid = 4096;  // upper bound on co-resident workgroups the workspace is sized for
 // Workspace layout: [0, 256) header, then the exchange units. The header holds the sticky flag word
-// (byte 0), the exchange-flag epoch (byte 64), the count of row-team workgroups that finished the
-// current launch (byte 128) and the 64-bit arrival ticket counter (byte 192), each on its own cache
-// line. A zero-filled header is the initial state.
+// (byte 0), the exchange-flag epoch (byte 64) and the count of row-team workgroups that finished the
+// current launch (byte 128), each on its own cache line. A zero-filled header is the initial state.
 constexpr size_t kHeaderBytes = 256;
 constexpr int kEpochWord = 16;   // uint32 index of the epoch in the header
 constexpr int kDoneWord = 32;    // uint32 index of the finished-workgroup count
-constexpr int kArriveQword = 24; // uint64 index of the arrival ticket counter
 // Three stages per team: exchange 1 alternates between stages 0 and 1 by row-iteration parity (a
 // member that moves on to its next row must not overwrite a value a slower member of the team has yet
 // to read), exchange 2 uses stage 2.
