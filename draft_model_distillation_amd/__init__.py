@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     library_path,
     load_library,
     opd_fused_fwd_bwd_verify,
+    opd_fused_fwd_bwd_verify_noalloc,
     opd_loss_bwd,
     opd_loss_fwd,
     pack_first_fit,

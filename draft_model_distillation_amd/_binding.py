@@ -27,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "opd_loss_bwd",
     "verify_accept_len",
     "opd_fused_fwd_bwd_verify",
+    "opd_fused_fwd_bwd_verify_noalloc",
     "opd_read_flags",
     "opd_length_head_loss",
     "opd_verify_sample",
@@ -85,6 +86,9 @@ def load_library(require_torch_runtime: bool = True) -> ctypes.CDLL:
         lib.opd_fused_fwd_bwd_verify.restype = i32
         lib.opd_fused_fwd_bwd_verify.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(OpdBlocks), f32, f32,
                                                  vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, sz, vp]
+        lib.opd_fused_fwd_bwd_verify_noalloc.restype = i32
+        lib.opd_fused_fwd_bwd_verify_noalloc.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(OpdBlocks), f32,
+                                                         f32, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp]
         lib.opd_read_flags.restype = i32
         lib.opd_read_flags.argtypes = [vp, sz, i32, ctypes.POINTER(ctypes.c_uint32), vp]
         lib.opd_length_head_loss.restype = i32
@@ -656,3 +660,33 @@ def opd_fused_fwd_bwd_verify(z, y, offsets, lengths, alpha: float, tau: float, g
     _check("opd_fused_fwd_bwd_verify", st)
     return o
 
+
+def opd_fused_fwd_bwd_verify_noalloc(z, y, offsets, lengths, alpha: float, tau: float, out: dict, grad_loss=None):
+    """opd_fused_fwd_bwd_verify without a workspace argument and without allocating: the library's
+    own per-GPU workspace array is used, and every output comes preallocated in ``out`` (keys loss,
+    target_top1, draft_top1, row_stats, dz, accept_len). Calls that overlap on one GPU must not be
+    made (they share that array)."""
+    torch = _torch()
+    zp, yp, rows, vocab, ld, dt = _logit_pair(z, y)
+    blocks, n_blocks = _blocks_checked(offsets, lengths, required=False)
+    _vector(grad_loss, "grad_loss", rows, torch.float32, optional=True)
+    _row_outputs(out, rows, n_blocks, ("loss", "target_top1", "draft_top1", "row_stats", "accept_len"))
+    _require(out.get("dz") is not None, "out['dz'] is missing")
+    _dtype_code(out["dz"])
+    _, rows_d, vocab_d, _ = _matrix(out["dz"], "dz", whole_vectors=False)
+    _require((rows_d, vocab_d) == (rows, vocab), f"dz must be [{rows}, {vocab}], got {tuple(out['dz'].shape)}")
+    _no_overlap(out["dz"], z, "dz", "z")
+    _no_overlap(out["dz"], y, "dz", "y")
+    _require(n_blocks == 0 or out.get("draft_top1") is not None, "draft_top1 is needed for verification")
+    dev = z.device
+    _same_device(dev, [("y", y), ("offsets", offsets), ("L", lengths), ("grad_loss", grad_loss)]
+                 + [(k, out.get(k)) for k in ("loss", "target_top1", "draft_top1", "row_stats", "dz", "accept_len")])
+    lib = load_library()
+    dzp, _, _, ld_dz = _matrix(out["dz"], "dz", whole_vectors=False)
+    st = lib.opd_fused_fwd_bwd_verify_noalloc(
+        zp, yp, dt, rows, vocab, ld, ctypes.byref(blocks) if blocks is not None else None,
+        float(alpha), float(tau), _ptr(grad_loss), out["loss"].data_ptr(), out["target_top1"].data_ptr(),
+        _ptr(out["draft_top1"]), out["row_stats"].data_ptr(), dzp, _dtype_code(out["dz"]), ld_dz,
+        out["accept_len"].data_ptr() if n_blocks else None, _stream(dev))
+    _check("opd_fused_fwd_bwd_verify_noalloc", st)
+    return out

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libopd_mi355x.so"
-SOURCES = ["opd_kernels.hip", "opd_epilogue.hip", "opd_sample.hip", "opd_api.cpp", "opd_pack.cpp", "opd_lmhead.cpp"]
+SOURCES = ["opd_kernels.hip", "opd_epilogue.hip", "opd_sample.hip", "opd_noalloc.hip", "opd_api.cpp", "opd_pack.cpp",
+           "opd_lmhead.cpp"]
 # Row kernels only: the VALU runs with the IEEE mode bit clear, so max/min need no NaN-quieting
 # canonicalisation of their operands (inputs are finite by contract). The host file keeps IEEE NaN
 # semantics for its argument checks, and the epilogue file the device library's accurate exp/log.

@@ -18,7 +18,7 @@ import sys
 from . import build as _build
 
 HOST_SOURCES = ["opd_api.cpp", "opd_pack.cpp", "opd_lmhead.cpp"]
-DEVICE_OBJECTS = ["opd_kernels.hip.o", "opd_epilogue.hip.o", "opd_sample.hip.o"]
+DEVICE_OBJECTS = ["opd_kernels.hip.o", "opd_epilogue.hip.o", "opd_sample.hip.o", "opd_noalloc.hip.o"]
 SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
 OUT_DIR = os.path.join(_build.PKG, "_build", "sanitized")
 LIBNAME = "libopd_mi355x_san.so"

@@ -153,6 +153,24 @@ opd_status_t opd_fused_fwd_bwd_verify(const void* z, const void* y, opd_dtype_t 
                                       hipStream_t stream);
 
 /*
+ * opd_fused_fwd_bwd_verify for callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation, arguments
+ * and results, without the workspace arguments. The workspace is a fixed array of
+ * opd_workspace_size() bytes inside the library (one per GPU, held until the process ends, zeroed
+ * by the first call on each GPU); the call makes no allocation of its own. Every call on a GPU
+ * shares that GPU's array, so calls that overlap on one GPU (e.g. on two streams at once) race and
+ * must not be made. The array covers every problem size the regular call accepts (a launch uses
+ * at most 4096 row-team workgroups); sizes the regular call rejects are rejected the same way.
+ * Device flags accumulate in the array and are reported by check mode (opd_set_check / OPD_CHECK=1).
+ */
+opd_status_t opd_fused_fwd_bwd_verify_noalloc(const void* z, const void* y, opd_dtype_t dt, int64_t n_rows,
+                                              int64_t vocab, int64_t ld, const opd_blocks_t* blocks,
+                                              float alpha, float tau, const float* grad_loss, float* loss,
+                                              int32_t* target_top1, int32_t* draft_top1, float* row_stats,
+                                              void* dz, opd_dtype_t dz_dt, int64_t ld_dz,
+                                              int32_t* accept_len, hipStream_t stream);
+
+/*
  * Length-head epilogue of verification ("AdaFlash: Adaptive Speculative Decoding with Online
  * Self-Improvement for High-Concurrency LLM Inference", section "2. Adaptive Length Head for
  * Token-Level Variance": the head predicts a draft block's acceptance rate, and the true rate after
