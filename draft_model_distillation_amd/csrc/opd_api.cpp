@@ -40,7 +40,7 @@ std::unordered_map<const void*, uint64_t> g_ws_gen;
 // reads the workspace's sticky flag word and returns OPD_ERR_DEVICE if a bit is set.
 std::atomic<int> g_check{-1};
 
-constexpr int64_t kMaxVocab = 1 << 19;  // 524,288 logits per row
+constexpr int64_t kMaxVocab = opd::kMaxVocab;
 
 opd_status_t fail(opd_status_t s, const std::string& msg) {
   g_last_error = msg;

@@ -12,7 +12,7 @@
 namespace opd {
 
 constexpr int kThreads = 256;  // workgroup size of every row kernel (4 wave64)
-constexpr int kStage1Units = 7;
+constexpr int kStage1Units = 5;  // values per member in exchange 1 (at most): top-1 mode's maxima, indices, z at y's
 constexpr int kStage2Units = 5;  // S, clipped sum, lowest indices of the row maxima of z and y, z at the latter
 constexpr int kMaxGrid = 4096;  // upper bound on co-resident workgroups the workspace is sized for
 // Workspace layout: [0, 256) header, then the exchange units. The header holds the sticky flag word
@@ -38,6 +38,7 @@ constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 // zeroes every exchange unit (no flag of the range that ends can then match a stale unit).
 constexpr uint32_t kEpochRestart = 0x40000000u;
 constexpr int kMaxTeamSize = 128;
+constexpr int kMaxVocab = 1 << 19;  // 524,288 logits per row
 
 enum Mode : int { kFused = 0, kForward = 1, kTop1 = 2 };
 

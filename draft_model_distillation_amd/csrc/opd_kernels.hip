@@ -94,7 +94,7 @@ struct F32In {
 
 struct BF16In {
   static constexpr int EPV = 8;
-  static constexpr int kWavesPerEU = 5;
+  static constexpr int kWavesPerEU = 6;  // 80 VGPRs and 26,844 B of LDS (53 allocation granules): 6 workgroups per CU
   static constexpr uint32_t kSentinel = 0xC700C700u;  // two bf16 -32768 (see F32In)
   __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
   __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -282,8 +282,9 @@ __device__ __forceinline__ void publish(uint64_t* units, int lane, uint32_t flag
 }
 
 // LDS shared by the waves of a workgroup (the chunk of y lives in its own array).
+template <int RX>
 struct Shared {
-  uint32_t rx[kMaxTeamSize * kStage1Units];  // gathered member values (wave 0)
+  uint32_t rx[RX];  // gathered member values (wave 0)
   uint32_t part[8];  // this chunk's values to publish
   float wred[4][4];  // per-wave partials
   int widx[4][2];    // per-wave first argmax of z and y
@@ -301,51 +302,61 @@ enum RowSlot : int {
 
 // ---------------------------------------------------------------- wave reductions (DPP)
 
-// Full-wave reductions on the DPP crossbar (quad_perm, row mirrors, row broadcasts): six ALU ops
-// instead of six LDS-permute round trips. The result is read from lane 63 and is wave-uniform.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ int dpp_mov(int v, int identity) {
-  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWS, 0xF, false);
+// Full-wave reductions: four in-row steps on the DPP crossbar (quad_perm, half-row and row mirrors),
+// each folded by the compiler into one VALU op with a DPP source (the move's old value is left
+// undefined: every lane of these patterns has a valid source), then the two cross-row steps with the
+// gfx950 lane swaps (v_permlane32_swap: halves of the wave; v_permlane16_swap: rows within each half).
+// Every lane ends with the result; it is read from the first active lane.
+template <int CTRL>
+__device__ __forceinline__ int dpp_row(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
-__device__ __forceinline__ float dppf(float v, float id, int which) {
-  switch (which) {
-    case 0: return __int_as_float(dpp_mov<0xB1, 0xF>(__float_as_int(v), __float_as_int(id)));
-    case 1: return __int_as_float(dpp_mov<0x4E, 0xF>(__float_as_int(v), __float_as_int(id)));
-    case 2: return __int_as_float(dpp_mov<0x141, 0xF>(__float_as_int(v), __float_as_int(id)));
-    case 3: return __int_as_float(dpp_mov<0x140, 0xF>(__float_as_int(v), __float_as_int(id)));
-    case 4: return __int_as_float(dpp_mov<0x142, 0xA>(__float_as_int(v), __float_as_int(id)));
-    default: return __int_as_float(dpp_mov<0x143, 0xC>(__float_as_int(v), __float_as_int(id)));
-  }
+__device__ __forceinline__ void swap32(int v, int& a, int& b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  a = (int)p[0];
+  b = (int)p[1];
 }
-__device__ __forceinline__ int dppi(int v, int id, int which) {
-  switch (which) {
-    case 0: return dpp_mov<0xB1, 0xF>(v, id);
-    case 1: return dpp_mov<0x4E, 0xF>(v, id);
-    case 2: return dpp_mov<0x141, 0xF>(v, id);
-    case 3: return dpp_mov<0x140, 0xF>(v, id);
-    case 4: return dpp_mov<0x142, 0xA>(v, id);
-    default: return dpp_mov<0x143, 0xC>(v, id);
-  }
+__device__ __forceinline__ void swap16(int v, int& a, int& b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  a = (int)p[0];
+  b = (int)p[1];
 }
 __device__ __forceinline__ float uniform_f(float v) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
-// max and min are idempotent: lanes a broadcast step leaves out may keep their own value as the
-// "old" operand, which saves the identity move of every step.
 __device__ __forceinline__ float wmax(float v) {
-#pragma unroll
-  for (int s = 0; s < 6; ++s) v = fmaxf(v, dppf(v, v, s));
-  return uniform_f(v);
+  v = fmaxf(v, __int_as_float(dpp_row<0xB1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_row<0x4E>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_row<0x141>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_row<0x140>(__float_as_int(v))));
+  int a, b;
+  swap32(__float_as_int(v), a, b);
+  v = fmaxf(__int_as_float(a), __int_as_float(b));
+  swap16(__float_as_int(v), a, b);
+  return uniform_f(fmaxf(__int_as_float(a), __int_as_float(b)));
 }
+// Fixed order: ((row 0 + row 2) + (row 1 + row 3)) of the in-row sums, the same on every call.
 __device__ __forceinline__ float wsum(float v) {
-#pragma unroll
-  for (int s = 0; s < 6; ++s) v = v + dppf(v, 0.f, s);
-  return uniform_f(v);
+  v = v + __int_as_float(dpp_row<0xB1>(__float_as_int(v)));
+  v = v + __int_as_float(dpp_row<0x4E>(__float_as_int(v)));
+  v = v + __int_as_float(dpp_row<0x141>(__float_as_int(v)));
+  v = v + __int_as_float(dpp_row<0x140>(__float_as_int(v)));
+  int a, b;
+  swap32(__float_as_int(v), a, b);
+  v = __int_as_float(a) + __int_as_float(b);
+  swap16(__float_as_int(v), a, b);
+  return uniform_f(__int_as_float(a) + __int_as_float(b));
 }
 __device__ __forceinline__ int wmin(int v) {
-#pragma unroll
-  for (int s = 0; s < 6; ++s) v = min(v, dppi(v, v, s));
-  return __builtin_amdgcn_readlane(v, 63);
+  v = min(v, dpp_row<0xB1>(v));
+  v = min(v, dpp_row<0x4E>(v));
+  v = min(v, dpp_row<0x141>(v));
+  v = min(v, dpp_row<0x140>(v));
+  int a, b;
+  swap32(v, a, b);
+  v = min(a, b);
+  swap16(v, a, b);
+  return __builtin_amdgcn_readfirstlane(min(a, b));
 }
 
 // ---------------------------------------------------------------- per-row constants
@@ -522,14 +533,21 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
   constexpr int EPV = In::EPV;
   constexpr int VB = EPV * (OutBF16 ? 2 : 4);  // dz bytes per input vector
   constexpr bool kSums = MODE != kTop1;
-  __shared__ Shared sh;
+  // Members of a team at most (the widest row, 2^19 logits, in chunks of K * 256 vectors), each with
+  // up to kStage1Units values: the gather buffer is sized for this instantiation only, so that a bf16
+  // workgroup with K = 5 stays within 53 LDS allocation granules (27,136 B) and six fit on a CU.
+  constexpr int kMaxG = (kMaxVocab / EPV + K * kThreads - 1) / (K * kThreads) < kMaxTeamSize
+                            ? (kMaxVocab / EPV + K * kThreads - 1) / (K * kThreads) : kMaxTeamSize;
+  __shared__ Shared<kMaxG * kStage1Units> sh;
   // The row chunk of y lives in LDS, z in VGPRs: this keeps the register footprint within 5
   // workgroups per CU (more resident teams hide the exchange waits). Each lane only ever reads back
   // its own 16 bytes.
   __shared__ uint4 ylds[K * kThreads];
   __shared__ VecMax<EPV> vmlds[K * kThreads];  // per-vector maxima from phase A to phase B
   const int tid = thread_id();
-  const int wave = tid >> 6;
+  // the wave index lives in a scalar register; per-row lane indices are rebuilt from it and the lane
+  // number (mbcnt) instead of keeping the work-item id in a vector register for the whole kernel
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Consecutive workgroups form a team, so its members land on different XCDs (round-robin dispatch)
   // and the five workgroups sharing a CU belong to different teams. Forming teams in the order the
   // workgroups start instead (a ticket counter in the workspace) measured 4-10 % slower: the start
@@ -584,7 +602,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     // The ln index is made opaque once per row: otherwise the compiler hoists every per-slot and
     // per-element ln test (sentinels, validity, offsets) out of the row loop and keeps them all
     // live in registers.
-    int lt = tid;
+    int lt = (wave << 6) + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     __asm__ volatile("" : "+v"(lt));
     const int voff = lt * 16;
     const int ln = lt & 63, wv = lt >> 6;
@@ -780,6 +798,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     // values per member in exchange 1: maxima and sums (the top-1 indices follow in exchange 2), or
     // in top-1 mode the maxima and their lowest indices
     constexpr int NU1 = kSums ? 4 : kStage1Units;
+    constexpr int kMy = kSums ? 2 : 1;  // where a member's maximum of y sits among its NU1 values
     if (wave == 0) {
       {
         const float sz = (sh.wred[0][z0 + 2] + sh.wred[1][z0 + 2]) + (sh.wred[2][z0 + 2] + sh.wred[3][z0 + 2]);
@@ -795,13 +814,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
           }
         }
         if (ln == 0) {
-          sh.part[z0 + 0] = __float_as_uint(Mzc);
-          sh.part[z0 + 1] = __float_as_uint(sz);
-          sh.part[z0 + 2] = __float_as_uint(Myc);
-          sh.part[z0 + 3] = __float_as_uint(sy2);
-          sh.part[z0 + 4] = (uint32_t)ciz;
-          sh.part[z0 + 5] = (uint32_t)ciy;
-          sh.part[z0 + 6] = __float_as_uint(cza);
+          if constexpr (kSums) {
+            sh.part[z0 + 0] = __float_as_uint(Mzc);
+            sh.part[z0 + 1] = __float_as_uint(sz);
+            sh.part[z0 + 2] = __float_as_uint(Myc);
+            sh.part[z0 + 3] = __float_as_uint(sy2);
+          } else {
+            sh.part[z0 + 0] = __float_as_uint(Mzc);
+            sh.part[z0 + 1] = __float_as_uint(Myc);
+            sh.part[z0 + 2] = (uint32_t)ciz;
+            sh.part[z0 + 3] = (uint32_t)ciy;
+            sh.part[z0 + 4] = __float_as_uint(cza);
+          }
         }
       }
       if (G > 1) {
@@ -816,22 +840,22 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         int liz = kBig, liy = kBig;
         for (int c = ln; c < G; c += 64) {
           mz = fmaxf(mz, __uint_as_float(sh.rx[z0 + c * NU1 + 0]));
-          my = fmaxf(my, __uint_as_float(sh.rx[z0 + c * NU1 + 2]));
+          my = fmaxf(my, __uint_as_float(sh.rx[z0 + c * NU1 + kMy]));
         }
         Mz = wmax(mz);
         My = wmax(my);
         const float cHz = Mz * kLog2e, cHy = My * kLog2e;
         for (int c = ln; c < G; c += 64) {
           const uint32_t* u = sh.rx + z0 + c * NU1;
-          const float mzc = __uint_as_float(u[0]), myc = __uint_as_float(u[2]);
+          const float mzc = __uint_as_float(u[0]), myc = __uint_as_float(u[kMy]);
           if constexpr (kSums) {
             lsz = __builtin_fmaf(__uint_as_float(u[1]), exp2_fast(mzc * kLog2e - cHz), lsz);
             lsy = __builtin_fmaf(__uint_as_float(u[3]), exp2_fast(myc * kLog2e - cHy), lsy);
           } else {
-            if (mzc == Mz) liz = min(liz, (int)u[4]);
-            if (myc == My && (int)u[5] < liy) {
-              liy = (int)u[5];
-              lza = __uint_as_float(u[6]);
+            if (mzc == Mz) liz = min(liz, (int)u[2]);
+            if (myc == My && (int)u[3] < liy) {
+              liy = (int)u[3];
+              lza = __uint_as_float(u[4]);
             }
           }
         }
@@ -848,11 +872,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       } else {
         Mz = Mzc;
         My = Myc;
-        Sz = __uint_as_float(sh.part[z0 + 1]);
-        Sy = __uint_as_float(sh.part[z0 + 3]);
-        dtop = (int)sh.part[z0 + 4];
-        atop = (int)sh.part[z0 + 5];
-        za = __uint_as_float(sh.part[z0 + 6]);
+        if constexpr (kSums) {
+          Sz = __uint_as_float(sh.part[z0 + 1]);
+          Sy = __uint_as_float(sh.part[z0 + 3]);
+          dtop = atop = kBig;
+          za = 0.f;
+        } else {
+          dtop = (int)sh.part[z0 + 2];
+          atop = (int)sh.part[z0 + 3];
+          za = __uint_as_float(sh.part[z0 + 4]);
+        }
       }
       if (ln == 0) {
         sh.row[z0 + kRowMz] = Mz;
@@ -877,7 +906,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
 
     const float Mz = sh.row[z0 + kRowMz];
     if constexpr (MODE == kTop1) {
-      if (chunk == 0 && tid == 0) {
+      if (chunk == 0 && lt == 0) {
         pp->target_top1[row] = __float_as_int(sh.row[z0 + kRowAtop]);
         if (pp->draft_top1) pp->draft_top1[row] = __float_as_int(sh.row[z0 + kRowDtop]);
       }
@@ -902,6 +931,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         const float u = slow ? 0.f : sc;
         pe = __builtin_fmaf(u, ek[k], pe);
         pb = __builtin_fmaf(u, bk[k], pb);
+        fence_vals(pe, pb);  // the vector's scale is dead before the element-by-element path
         if (__builtin_amdgcn_ballot_w64(slow)) {
           opaque(zr[k]);
           float x[EPV], w[EPV];
@@ -1089,7 +1119,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       }
     }
   }
-  if (tid == 0) {
+  const int tid_end = (wave << 6) + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  if (tid_end == 0) {
     if (sh.err) atomicOr(P.flags, (uint32_t)kFlagSpinTimeout);
     // Device-mode flags: the last workgroup to finish advances the epoch for the next launch; by
     // then every workgroup of this launch has read it. Relaxed agent-scope atomics; the kernel
@@ -1111,11 +1142,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         // The range restarts: zero every exchange unit first, so that no unit written in the range
         // that ends can carry a flag of the next one. No other workgroup of this launch is left.
         constexpr size_t n_units = (kWorkspaceBytes - kHeaderBytes) / 8;
-        for (size_t i = tid; i < n_units; i += kThreads)
+        for (size_t i = tid_end; i < n_units; i += kThreads)
           __hip_atomic_store(P.units + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         next = 0;
       }
-      if (tid == 0) {
+      if (tid_end == 0) {
         __hip_atomic_store(P.flags + kDoneWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(P.flags + kEpochWord, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -1310,8 +1341,26 @@ hipError_t launch_team(const TeamParams& p, int mode, int in_bf16, int out_bf16,
 }
 
 hipError_t team_occupancy(int mode, int in_bf16, int out_bf16, int K, bool dev_flags, int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      blocks_per_cu, team_kernel_any(mode, in_bf16, out_bf16, K, dev_flags), kThreads, 0);
+  const void* fn = team_kernel_any(mode, in_bf16, out_bf16, K, dev_flags);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kThreads, 0);
+  if (e != hipSuccess) return e;
+  // The team kernels need every workgroup of the grid resident at once, so the count must not be
+  // optimistic. LDS is allocated in 512-byte granules; the runtime's count was seen to assume a
+  // finer allocation (a workgroup of 27,260 B was reported to fit six times in 160 KiB, where
+  // 6 x 27,648 B do not). Bound the count by the granule-rounded LDS per CU.
+  hipFuncAttributes attr;
+  e = hipFuncGetAttributes(&attr, fn);
+  if (e != hipSuccess) return e;
+  int dev = 0, lds_cu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev)) != hipSuccess)
+    return e;
+  const size_t lds = ((attr.sharedSizeBytes + 511) / 512) * 512;
+  if (lds > 0 && lds_cu > 0) {
+    const int by_lds = (int)((size_t)lds_cu / lds);
+    if (by_lds < *blocks_per_cu) *blocks_per_cu = by_lds;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_bwd(const BwdParams& p, int in_bf16, int out_bf16, hipStream_t s) {
