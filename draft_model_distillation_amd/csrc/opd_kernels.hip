@@ -290,6 +290,9 @@ struct Shared {
   int widx[4][2];    // per-wave first argmax of z and y
   float wza[4];      // z at the wave's argmax of y
   float row[12];     // row constants, written by wave 0
+  float pend[5];     // forward mode, chunk 0: row constants of the row whose exchange 2 is pending
+  int pend_row;
+  uint32_t pend_flag;
   int err;
   int last;          // this workgroup is the last of the launch to finish (device-epoch launches)
   uint32_t fbase;    // first exchange flag of this launch
@@ -579,6 +582,66 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     sh.fbase = b + 1u;
   }
 
+  // Exchange 2 of one row, wave 0: combines the members' values (gathered into sh.rx, or this chunk's
+  // own when the row has one member) in a fixed order and, in chunk 0, writes the row's outputs.
+  // Returns S, the clipped sum and the target top-1 through sh.row for phase C.
+  auto finish_row = [&](KParams* pp, int r, bool gathered, int ln_, int z0_, float Mz_, float ln_sz_, float My_,
+                        float ln_sy_, float delta_, float alpha_) {
+    float S = __uint_as_float(sh.part[z0_ + 0]), rkl = __uint_as_float(sh.part[z0_ + 1]);
+    int dtop = (int)sh.part[z0_ + 2], atop = (int)sh.part[z0_ + 3];
+    float za = __uint_as_float(sh.part[z0_ + 4]);
+    if (gathered) {
+      float ls = 0.f, lr = 0.f, lza = 0.f;
+      int liz = kBig, liy = kBig;
+      for (int c = ln_; c < G; c += 64) {
+        const uint32_t* u = sh.rx + z0_ + c * kStage2Units;
+        ls += __uint_as_float(u[0]);
+        lr += __uint_as_float(u[1]);
+        liz = min(liz, (int)u[2]);
+        if ((int)u[3] < liy) {
+          liy = (int)u[3];
+          lza = __uint_as_float(u[4]);
+        }
+      }
+      S = wsum(ls);
+      rkl = wsum(lr);
+      dtop = wmin(liz);
+      atop = wmin(liy);
+      za = wsum(liy == atop ? lza : 0.f);
+    }
+    if (ln_ == 0) {
+      sh.row[z0_ + kRowS] = S;
+      sh.row[z0_ + kRowRkl] = rkl;
+      sh.row[z0_ + kRowAtop] = __int_as_float(atop);
+      if (chunk == 0) {
+        const float ce = (Mz_ - za) + ln_sz_;
+        float* st = pp->row_stats + 8 * (int64_t)r;
+        pp->loss[r] = alpha_ * rkl + (1.f - alpha_) * ce;
+        pp->target_top1[r] = atop;
+        if (pp->draft_top1) pp->draft_top1[r] = dtop;
+        st[0] = Mz_ + ln_sz_;
+        st[1] = My_ + ln_sy_;
+        st[2] = S;
+        st[3] = rkl;
+        st[4] = Mz_;
+        st[5] = ln_sz_;
+        st[6] = delta_;
+        st[7] = ce;
+      }
+    }
+  };
+  // Forward mode: no member needs the row's sums, so none waits for exchange 2; chunk 0 gathers a
+  // row's exchange 2 when its next row is about to publish exchange 1 (every member published its
+  // exchange 2 before starting the next row, so that gather does not wait), and after its last row.
+  // Exchange 2 keeps one stage: a member overwrites it only after gathering the next exchange 1,
+  // which includes chunk 0's, published after chunk 0 has read the pending values.
+  auto finish_pending = [&](KParams* pp, int ln_, int z0_) -> bool {
+    const bool ok = gather_wave<kStage2Units>(sh.rx + z0_, units2, G, ln_, sh.pend_flag, pp->spin_limit);
+    if (ok) finish_row(pp, sh.pend_row, true, ln_, z0_, sh.pend[0], sh.pend[1], sh.pend[2], sh.pend[3], sh.pend[4],
+                       pp->alpha);
+    return ok;
+  };
+
   int iter = 0;
   for (int row = team; row < P.n_rows; row += P.n_teams, ++iter) {
     __syncthreads();  // the previous row is done with ylds and sh
@@ -828,6 +891,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
           }
         }
       }
+      if constexpr (MODE == kForward) {
+        if (G > 1 && chunk == 0 && iter > 0 && !finish_pending(pp, ln, z0)) sh.err = 1;
+      }
       if (G > 1) {
         publish<NU1>(units1 + (size_t)chunk * 8, ln, flag1, sh.part + z0);
         if (!gather_wave<NU1>(sh.rx + z0, units1, G, ln, flag1, pp->spin_limit)) sh.err = 1;
@@ -1014,7 +1080,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       }
       __syncthreads();
       // ---- exchange 2 (wave 0) and the row outputs (chunk 0)
-      const bool need_all = (MODE == kFused) || chunk == 0;
       const uint32_t flag2 = flag1 + 1u;
       if (wave == 0) {
         if (ln == 0) {
@@ -1036,50 +1101,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         }
         if (G > 1) {
           publish<kStage2Units>(units2 + (size_t)chunk * 8, ln, flag2, sh.part + z0);
-          if (need_all && !gather_wave<kStage2Units>(sh.rx + z0, units2, G, ln, flag2, pp->spin_limit)) sh.err = 1;
+          if (MODE == kFused && !gather_wave<kStage2Units>(sh.rx + z0, units2, G, ln, flag2, pp->spin_limit)) sh.err = 1;
         }
-        float S = __uint_as_float(sh.part[z0 + 0]), rkl = __uint_as_float(sh.part[z0 + 1]);
-        int dtop = (int)sh.part[z0 + 2], atop = (int)sh.part[z0 + 3];
-        float za = __uint_as_float(sh.part[z0 + 4]);
-        if (G > 1 && need_all) {
-          float ls = 0.f, lr = 0.f, lza = 0.f;
-          int liz = kBig, liy = kBig;
-          for (int c = ln; c < G; c += 64) {
-            const uint32_t* u = sh.rx + z0 + c * kStage2Units;
-            ls += __uint_as_float(u[0]);
-            lr += __uint_as_float(u[1]);
-            liz = min(liz, (int)u[2]);
-            if ((int)u[3] < liy) {
-              liy = (int)u[3];
-              lza = __uint_as_float(u[4]);
-            }
-          }
-          S = wsum(ls);
-          rkl = wsum(lr);
-          dtop = wmin(liz);
-          atop = wmin(liy);
-          za = wsum(liy == atop ? lza : 0.f);
-        }
-        if (ln == 0) {
-          sh.row[z0 + kRowS] = S;
-          sh.row[z0 + kRowRkl] = rkl;
-          sh.row[z0 + kRowAtop] = __int_as_float(atop);
-          if (chunk == 0) {
-            const float My = sh.row[z0 + kRowMy], ln_sy = sh.row[z0 + kRowLnSy];
-            const float ce = (Mz - za) + ln_sz;
-            float* st = pp->row_stats + 8 * (int64_t)row;
-            pp->loss[row] = alpha * rkl + (1.f - alpha) * ce;
-            pp->target_top1[row] = atop;
-            if (pp->draft_top1) pp->draft_top1[row] = dtop;
-            st[0] = Mz + ln_sz;
-            st[1] = My + ln_sy;
-            st[2] = S;
-            st[3] = rkl;
-            st[4] = Mz;
-            st[5] = ln_sz;
-            st[6] = delta;
-            st[7] = ce;
-          }
+        if (MODE == kFused || G == 1) {
+          finish_row(pp, row, G > 1, ln, z0, Mz, ln_sz, sh.row[z0 + kRowMy], sh.row[z0 + kRowLnSy], delta, alpha);
+        } else if (chunk == 0 && ln == 0) {  // forward mode: gathered later (finish_pending)
+          sh.pend[0] = Mz;
+          sh.pend[1] = ln_sz;
+          sh.pend[2] = sh.row[z0 + kRowMy];
+          sh.pend[3] = sh.row[z0 + kRowLnSy];
+          sh.pend[4] = delta;
+          sh.pend_row = row;
+          sh.pend_flag = flag2;
         }
       }
       __syncthreads();
@@ -1117,6 +1150,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
           buf_store_vec<OutBF16, EPV>(rd, off, o);
         }
       }
+    }
+  }
+  if constexpr (MODE == kForward) {  // the last row's exchange 2
+    if (P.G > 1 && chunk == 0 && iter > 0 && wave == 0 && !sh.err) {
+      KParams* pp = (KParams*)__builtin_amdgcn_kernarg_segment_ptr();
+      const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      if (!finish_pending(pp, ln, 0)) sh.err = 1;
     }
   }
   const int tid_end = (wave << 6) + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
