@@ -557,7 +557,7 @@ def main():
                    # opd_verify_sample at T = 1 (all kernels) per call; gbs = z and y of the rows the
                    # verification reads, once, / time
                    "sampling_verify": sample,
-                   # opd_lmhead_fused_fwd_bwd_verify per call (three bf16 GEMMs through rocBLAS + the
+                   # opd_lmhead_fused_fwd_bwd_verify per call (three bf16 GEMMs on the library's MFMA kernels + the
                    # row kernel); gemm_tflops counts the GEMM flops only, against 2.5 PFLOP/s dense bf16
                    "lmhead_fused": lmhead,
                    # per workload: the fused call timed one call at a time with HIP events (median, p10,

@@ -109,7 +109,7 @@ def load_library(require_torch_runtime: bool = True) -> ctypes.CDLL:
         lib.opd_lmhead_fused_fwd_bwd_verify.restype = i32
         lib.opd_lmhead_fused_fwd_bwd_verify.argtypes = [vp, vp, i64, vp, i32, i64, i64, i64, ctypes.POINTER(OpdBlocks),
                                                         ctypes.c_float, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp,
-                                                        vp, sz, i64, vp, sz, vp]
+                                                        vp, vp, vp, sz, i64, vp, sz, vp]
         lib.opd_stream_probe.restype = i32
         lib.opd_stream_probe.argtypes = [vp, vp, vp, sz, vp]
         lib.opd_set_spin_limit.restype = None
@@ -563,14 +563,16 @@ def verify_sample(z, y, offsets, lengths, draft_tokens, u_accept, u_resample, te
 
 
 def lmhead_fused_fwd_bwd_verify(h, W, y, offsets, lengths, alpha: float, tau: float, grad_loss=None,
-                                chunk_rows: int = 2048, want_dh: bool = True, want_dW: bool = True, scratch=None,
-                                ws=None, out=None):
+                                chunk_rows: int = 2048, want_dh: bool = True, want_dW: bool = True,
+                                want_logit_stats: bool = True, scratch=None, ws=None, out=None):
     """OPD loss fused with the vocabulary projection z = h W^T (opd_lmhead_fused_fwd_bwd_verify).
 
     h [R, H] bf16, W [V, H] bf16, y [R, V] fp32 (rows may be padded to a 16-byte pitch). Returns a dict
-    with loss, target_top1, draft_top1, row_stats, accept_len (if blocks), dh [R, H] f32 and dW [V, H]
-    f32. ``out`` may hold preallocated tensors under the same keys and ``scratch`` a uint8 device
-    tensor of at least opd_lmhead_scratch_size bytes, so that repeated calls allocate nothing.
+    with loss, target_top1, draft_top1, row_stats, accept_len (if blocks), dh [R, H] f32, dW [V, H]
+    f32, and from the logits product's epilogue logit_max_lse [R, 2] f32 (max z, log-sum-exp z) and
+    logit_argmax [R] int32. ``out`` may hold preallocated tensors under the same keys and ``scratch``
+    a uint8 device tensor of at least opd_lmhead_scratch_size bytes, so that repeated calls allocate
+    nothing.
     """
     torch = _torch()
     yp, rows, vocab, ld = _matrix(y, "y")
@@ -589,10 +591,15 @@ def lmhead_fused_fwd_bwd_verify(h, W, y, offsets, lengths, alpha: float, tau: fl
             _rows_matrix(o["dh"], "dh", rows, hidden, torch.float32)
         if o.get("dW") is not None:
             _rows_matrix(o["dW"], "dW", vocab, hidden, torch.float32)
+        if o.get("logit_max_lse") is not None:
+            _rows_matrix(o["logit_max_lse"], "logit_max_lse", rows, 2, torch.float32)
+        if o.get("logit_argmax") is not None:
+            _vector(o["logit_argmax"], "logit_argmax", rows, torch.int32)
     dev = y.device
     _same_device(dev, [("h", h), ("W", W), ("offsets", offsets), ("L", lengths), ("grad_loss", grad_loss),
                        ("scratch", scratch)] + [(k, o.get(k)) for k in ("loss", "target_top1", "draft_top1",
-                                                                       "row_stats", "accept_len", "dh", "dW")])
+                                                                       "row_stats", "accept_len", "dh", "dW",
+                                                                       "logit_max_lse", "logit_argmax")])
     lib = load_library()
     ws = _workspace_arg(ws, dev)
     rc = max(1, min(int(chunk_rows), max(rows, 1)))
@@ -607,11 +614,14 @@ def lmhead_fused_fwd_bwd_verify(h, W, y, offsets, lengths, alpha: float, tau: fl
         o["accept_len"] = torch.empty(n_blocks, dtype=torch.int32, device=dev)
         o["dh"] = torch.empty(rows, hidden, dtype=torch.float32, device=dev) if want_dh else None
         o["dW"] = torch.empty(vocab, hidden, dtype=torch.float32, device=dev) if want_dW else None
+        o["logit_max_lse"] = torch.empty(rows, 2, dtype=torch.float32, device=dev) if want_logit_stats else None
+        o["logit_argmax"] = torch.empty(rows, dtype=torch.int32, device=dev) if want_logit_stats else None
     st = lib.opd_lmhead_fused_fwd_bwd_verify(
         h.data_ptr(), W.data_ptr(), hidden, yp, _dtype_code(y), rows, vocab, ld,
         ctypes.byref(blocks) if blocks is not None else None, float(alpha), float(tau), _ptr(grad_loss),
         o["loss"].data_ptr(), o["target_top1"].data_ptr(), _ptr(o["draft_top1"]), o["row_stats"].data_ptr(),
-        _ptr(o["dh"]), _ptr(o["dW"]), _ptr(o["accept_len"]) if n_blocks else None, scratch.data_ptr(),
+        _ptr(o["dh"]), _ptr(o["dW"]), _ptr(o.get("logit_max_lse")), _ptr(o.get("logit_argmax")),
+        _ptr(o["accept_len"]) if n_blocks else None, scratch.data_ptr(),
         scratch.numel() * scratch.element_size(), rc, ws.data_ptr(), ws.numel(), _stream(dev))
     _check("opd_lmhead_fused_fwd_bwd_verify", st)
     o["scratch"] = scratch

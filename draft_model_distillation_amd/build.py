@@ -2,8 +2,8 @@
 
     python -m draft_model_distillation_amd.build
 
-The library links the HIP runtime and rocBLAS (for the plain matrix products of the lm_head-fused
-path); the Python binding loads it with ctypes.
+The library links only the HIP runtime (every kernel, the matrix products of the lm_head-fused path
+included, is the library's own); the Python binding loads it with ctypes.
 """
 
 from __future__ import annotations
@@ -19,8 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libopd_mi355x.so"
-SOURCES = ["opd_kernels.hip", "opd_epilogue.hip", "opd_sample.hip", "opd_noalloc.hip", "opd_api.cpp", "opd_pack.cpp",
-           "opd_lmhead.cpp"]
+SOURCES = ["opd_kernels.hip", "opd_epilogue.hip", "opd_sample.hip", "opd_noalloc.hip", "opd_gemm.hip", "opd_api.cpp",
+           "opd_pack.cpp", "opd_lmhead.cpp"]
 # Row kernels only: the VALU runs with the IEEE mode bit clear, so max/min need no NaN-quieting
 # canonicalisation of their operands (inputs are finite by contract). The host file keeps IEEE NaN
 # semantics for its argument checks, and the epilogue file the device library's accurate exp/log.
@@ -71,7 +71,7 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     out = lib_path()
     tmp = out + ".tmp"
-    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-L/opt/rocm/lib", "-lrocblas",
+    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-L/opt/rocm/lib",
            "-Wl,-rpath,/opt/rocm/lib", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)

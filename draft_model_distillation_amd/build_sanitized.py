@@ -3,7 +3,7 @@
     python -m draft_model_distillation_amd.build_sanitized
 
 The host sources (argument checks, launch planning, exchange-flag bookkeeping, the packer, the
-rocBLAS calls) are compiled with g++ and both sanitizers; the device code is taken unchanged from the
+matrix-product planning) are compiled with g++ and both sanitizers; the device code is taken unchanged from the
 regular build's objects. The result is a separate library under ``_build/sanitized/`` that the CPU
 tests load in a child process (with the sanitizer runtimes preloaded into Python) in place of the
 regular one; device code is never instrumented.
@@ -18,7 +18,7 @@ import sys
 from . import build as _build
 
 HOST_SOURCES = ["opd_api.cpp", "opd_pack.cpp", "opd_lmhead.cpp"]
-DEVICE_OBJECTS = ["opd_kernels.hip.o", "opd_epilogue.hip.o", "opd_sample.hip.o", "opd_noalloc.hip.o"]
+DEVICE_OBJECTS = ["opd_kernels.hip.o", "opd_epilogue.hip.o", "opd_sample.hip.o", "opd_noalloc.hip.o", "opd_gemm.hip.o"]
 SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
 OUT_DIR = os.path.join(_build.PKG, "_build", "sanitized")
 LIBNAME = "libopd_mi355x_san.so"
@@ -52,7 +52,7 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"g++ failed for {src}:\n{r.stdout}\n{r.stderr}")
         objs.append(obj)
     out = os.path.join(OUT_DIR, LIBNAME)
-    cmd = ["g++", "-shared", *SAN_FLAGS, *objs, *dev_objs, "-L/opt/rocm/lib", "-lamdhip64", "-lrocblas",
+    cmd = ["g++", "-shared", *SAN_FLAGS, *objs, *dev_objs, "-L/opt/rocm/lib", "-lamdhip64",
            "-Wl,-rpath,/opt/rocm/lib", "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)

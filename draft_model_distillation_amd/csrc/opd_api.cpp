@@ -6,6 +6,7 @@
 
 #include "opd.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdio>
@@ -508,9 +509,12 @@ static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 size_t opd_lmhead_scratch_size(int64_t chunk_rows, int64_t vocab, int64_t ld_y) {
   if (chunk_rows <= 0 || vocab <= 0 || ld_y < vocab) return 0;
-  // logits chunk: fp32 with the pitch of y (the row kernel reads both with one pitch); dz chunk: bf16
+  // logits chunk: fp32 with the pitch of y (the row kernel reads both with one pitch); dz chunk: bf16,
+  // a region that first holds the logits product's row-statistics partials (3 floats per row and
+  // 128-column half tile)
   const int64_t zb = round_up(chunk_rows * ld_y * 4, 256);
-  const int64_t db = round_up(chunk_rows * round_up(vocab, 8) * 2, 256);
+  const int64_t parts = 2 * ((vocab + opd::kGemmTile - 1) / opd::kGemmTile);
+  const int64_t db = round_up(std::max(chunk_rows * round_up(vocab, 8) * 2, chunk_rows * parts * 12), 256);
   return (size_t)(zb + db);
 }
 
@@ -519,8 +523,9 @@ static opd_status_t opd_lmhead_fused_fwd_bwd_verify_impl(const void* h, const vo
                                              const opd_blocks_t* blocks, float alpha, float tau,
                                              const float* grad_loss, float* loss, int32_t* target_top1,
                                              int32_t* draft_top1, float* row_stats, float* dh, float* dW,
-                                             int32_t* accept_len, void* scratch, size_t scratch_bytes,
-                                             int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                             float* logit_max_lse, int32_t* logit_argmax, int32_t* accept_len,
+                                             void* scratch, size_t scratch_bytes, int64_t chunk_rows, void* ws,
+                                             size_t ws_bytes, hipStream_t stream) {
   opd_status_t s = check_logits(y, y, dt_y, n_rows, vocab, ld_y);
   if (s != OPD_OK) return s;
   if (dt_y != OPD_F32) return fail(OPD_ERR_DTYPE, "y must be fp32 (the logits chunk it is paired with is fp32)");
@@ -552,27 +557,47 @@ static opd_status_t opd_lmhead_fused_fwd_bwd_verify_impl(const void* h, const vo
   const int64_t ld_dz = round_up(vocab, 8);
   float* zc = static_cast<float*>(scratch);
   uint16_t* dzc = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(scratch) + round_up(rc_max * ld_y * 4, 256));
+  // The dz region holds the logits product's row-statistics partials until the row kernel writes dz
+  // (rc x 2 ceil(V / 256) x 3 floats, well under rc x ld_dz bf16), and the logits region holds the
+  // split dh product's partials once the row kernel has read the logits (k_split x rc x hidden floats).
+  float* zstats = reinterpret_cast<float*>(dzc);
+  const bool want_stats = logit_max_lse || logit_argmax;
+  const int n_parts = 2 * (int)((vocab + opd::kGemmTile - 1) / opd::kGemmTile);
+  const uint16_t* Wb = static_cast<const uint16_t*>(W);
   const uint8_t* hb = static_cast<const uint8_t*>(h);
   const uint8_t* yb = static_cast<const uint8_t*>(y);
-  // Row-major matrices seen column-major: h^T [hidden x rows], W^T [hidden x vocab], z^T [vocab x rows].
   for (int64_t r0 = 0; r0 < n_rows; r0 += chunk_rows) {
     const int64_t rc = (n_rows - r0) < chunk_rows ? (n_rows - r0) : chunk_rows;
-    const void* hc = hb + r0 * hidden * 2;
-    // z^T = W h^T  (vocab x rc)
-    if ((s = opd::gemm_bf16_f32(true, false, vocab, rc, hidden, W, hidden, hc, hidden, 0.f, zc, ld_y, stream)) != OPD_OK)
+    const uint16_t* hc = reinterpret_cast<const uint16_t*>(hb + r0 * hidden * 2);
+    // z [rc, V] = h_c W^T, with the per-row max / argmax / log-sum-exp in the product's epilogue
+    if ((s = opd::gemm_bf16_f32(hc, hidden, true, Wb, hidden, true, rc, vocab, hidden, 0.f, zc, ld_y, 1, nullptr,
+                                want_stats ? zstats : nullptr, stream)) != OPD_OK)
       return s;
+    if (want_stats) {
+      hipError_t e = opd::launch_zstats_reduce(zstats, n_parts, (int)rc, logit_max_lse ? logit_max_lse + 2 * r0 : nullptr,
+                                               logit_argmax ? logit_argmax + r0 : nullptr, stream);
+      if (e != hipSuccess) return hip_fail(e, "logits statistics");
+    }
     if ((s = run_team(opd::kFused, zc, yb + r0 * ld_y * 4, OPD_F32, rc, vocab, ld_y, alpha, tau,
                       grad_loss ? grad_loss + r0 : nullptr, loss + r0, target_top1 + r0,
                       draft_top1 ? draft_top1 + r0 : nullptr, row_stats + 8 * r0, dzc, OPD_BF16, ld_dz, ws,
                       stream)) != OPD_OK)
       return s;
-    // dh^T = W^T dz^T  (hidden x rc)
-    if (dh && (s = opd::gemm_bf16_f32(false, false, hidden, rc, vocab, W, hidden, dzc, ld_dz, 0.f, dh + r0 * hidden,
-                                      hidden, stream)) != OPD_OK)
-      return s;
-    // dW^T (+)= h^T dz  (hidden x vocab), accumulated over the chunks
-    if (dW && (s = opd::gemm_bf16_f32(false, true, hidden, vocab, rc, hc, hidden, dzc, ld_dz, r0 == 0 ? 0.f : 1.f, dW,
-                                      hidden, stream)) != OPD_OK)
+    // dh [rc, hidden] = dz W: K = V is long and the output small, so K is split over workgroup
+    // slices (enough to give every CU a tile, as far as the logits region holds the partials)
+    if (dh) {
+      const int64_t tiles = ((rc + 255) / 256) * ((hidden + 255) / 256);
+      int64_t split = (256 + tiles - 1) / tiles;
+      split = std::min<int64_t>(split, std::max<int64_t>(1, ld_y / hidden));
+      split = std::min<int64_t>(split, std::max<int64_t>(1, vocab / 1024));
+      split = std::min<int64_t>(split, 32);
+      if ((s = opd::gemm_bf16_f32(dzc, ld_dz, true, Wb, hidden, false, rc, hidden, vocab, 0.f, dh + r0 * hidden, hidden,
+                                  (int)split, zc, nullptr, stream)) != OPD_OK)
+        return s;
+    }
+    // dW [V, hidden] (+)= dz^T h_c, accumulated over the chunks
+    if (dW && (s = opd::gemm_bf16_f32(dzc, ld_dz, false, hc, hidden, false, vocab, hidden, rc, r0 == 0 ? 0.f : 1.f,
+                                      dW, hidden, 1, nullptr, nullptr, stream)) != OPD_OK)
       return s;
   }
   return run_accept(blocks, n_rows, draft_top1, target_top1, accept_len, ws, stream);
@@ -671,12 +696,13 @@ opd_status_t opd_lmhead_fused_fwd_bwd_verify(const void* h, const void* W, int64
                                              const opd_blocks_t* blocks, float alpha, float tau,
                                              const float* grad_loss, float* loss, int32_t* target_top1,
                                              int32_t* draft_top1, float* row_stats, float* dh, float* dW,
-                                             int32_t* accept_len, void* scratch, size_t scratch_bytes,
-                                             int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                             float* logit_max_lse, int32_t* logit_argmax, int32_t* accept_len,
+                                             void* scratch, size_t scratch_bytes, int64_t chunk_rows, void* ws,
+                                             size_t ws_bytes, hipStream_t stream) {
   return finish(opd_lmhead_fused_fwd_bwd_verify_impl(h, W, hidden, y, dt_y, n_rows, vocab, ld_y, blocks, alpha, tau,
                                                      grad_loss, loss, target_top1, draft_top1, row_stats, dh, dW,
-                                                     accept_len, scratch, scratch_bytes, chunk_rows, ws, ws_bytes,
-                                                     stream),
+                                                     logit_max_lse, logit_argmax, accept_len, scratch, scratch_bytes,
+                                                     chunk_rows, ws, ws_bytes, stream),
                 ws, stream);
 }
 

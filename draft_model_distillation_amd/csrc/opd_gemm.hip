@@ -1,0 +1,573 @@
+// bf16 matrix products on the gfx950 matrix cores for the lm_head-fused OPD loss (opd_api.cpp):
+//   logits   z[R, V]  = h[R, H] W[V, H]^T      (both operands K-major)
+//   dh       dh[R, H] = dz[R, V] W[V, H]       (dz K-major, W N-major; split over K = V)
+//   dW       dW[V, H] = dz[R, V]^T h[R, H]     (both operands M/N-major)
+// which the loss of "AdaFlash: Adaptive Speculative Decoding with Online Self-Improvement for
+// High-Concurrency LLM Inference", section "1. On-Policy Distillation (OPD) for Domain Adaptation",
+// needs when the drafter's vocabulary projection is trained with it.
+//
+// One kernel template: C[m, n] = sum_k A(m, k) B(k, n) (+ beta C), bf16 operands, fp32 accumulation
+// with v_mfma_f32_32x32x16_bf16. Workgroup tile 256 x 256, four waves of 128 x 128 (4 x 4 blocks of
+// 32 x 32: 256 accumulators per lane, all in the accumulation registers), one workgroup per CU. Each
+// operand tile is staged in LDS as [m or n][k] with rows of BK bf16 whose 16-byte k vectors are
+// XOR-swizzled by the row, so that fragment reads and tile writes spread over the LDS banks.
+//   K-major operand (global [m][K]): loaded straight into LDS (buffer loads with the LDS-DMA bit:
+//   lane l of an instruction fills 16 bytes at l * 16), the lanes choosing their global vector so that
+//   the linear LDS image is the swizzled tile. No registers, no LDS write instructions.
+//   M/N-major operand (global [K][m]): 16-byte loads along m into registers; each thread holds 8 k x
+//   8 m values and writes them transposed (byte permutes, 16-byte LDS writes) between the products.
+// K step 64 and two LDS stages: the loads of step s + 1 are issued during step s (one per product of
+// its first k slice). A ring of four 32-wide stages (loads three steps ahead) is also implemented for
+// the both-K-major product, but measured slower. A partial K step (K not a multiple of the step) is
+// loaded through registers with the values past K zeroed and runs first, so that every step goes
+// through the same pipeline.
+// MFMA operand fragments (lane l: row l % 32, k = 8 (l / 32) + 0..7) are single 16-byte LDS reads.
+// Optional epilogue (the logits product): per row and per 128-column half tile, the maximum, the lowest
+// column index holding it and the sum of exp(c - max), written as partials that k_zstats_reduce
+// combines in a fixed order into per-row max, argmax and log-sum-exp.
+
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "opd_internal.h"
+
+namespace opd {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, BN = 256;
+constexpr int kGemmThreads = 256;
+constexpr int kLdsBytes = 128 * 1024;  // either configuration: 4 x 32 KiB or 2 x 64 KiB
+
+// K step of the products with both operands K-major: 64 with two stages measured faster on the logits
+// product (2048 x 151936 x 4096) than 32 with a ring of four (2.6 vs 3.1 ms); both are supported.
+constexpr int kBothKmajorStep = 64;
+
+// Pipeline shape of a product: K step, stages in the LDS ring, and the derived sizes.
+template <bool A_KMAJOR, bool B_KMAJOR>
+struct Cfg {
+  static constexpr bool kDmaBoth = A_KMAJOR && B_KMAJOR;
+  static constexpr int BK = kDmaBoth ? kBothKmajorStep : 64;
+  static constexpr int kStages = kDmaBoth && BK == 32 ? 4 : 2;
+  static constexpr int kAhead = kStages - 1;             // steps loaded ahead
+  static constexpr int kRowBytes = 2 * BK;               // one LDS tile row
+  static constexpr int kTileBytes = 256 * kRowBytes;     // one operand tile
+  static constexpr int kStageBytes = 2 * kTileBytes;     // A and B
+  static constexpr int kVecs = BK / 8;                   // 16-byte vectors per thread per operand tile
+  static constexpr int kSlices = BK / 16;                // 16-wide k slices per step
+  static constexpr int kRowVecs = BK / 8;                // 16-byte vectors per tile row
+  static constexpr int kInstrRows = 1024 / kRowBytes;    // tile rows one LDS-DMA instruction fills
+  static_assert(kStages * kStageBytes == kLdsBytes, "LDS ring size");
+  static_assert(kDmaBoth || BK == 64, "register-held (transposed) tiles assume a K step of 64");
+};
+
+// LDS position of k vector kv of tile row `row`: 16-byte slot kv ^ swz(row). The LDS serves 16 lanes'
+// 16-byte accesses per cycle from 64 four-byte banks: 16 bank groups of 16 bytes, group
+// (row * kRowVecs + slot) % 16. 64-byte rows (BK 32): (row >> 2) & 3 makes the fragment reads
+// (16 consecutive rows, one k vector) conflict-free. 128-byte rows (BK 64): ((row >> 1) ^ (row >> 4))
+// & 7 makes them conflict-free and keeps the transposed writes of an M/N-major operand (rows 8 g + o
+// for 16 consecutive g) at most 2-way.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (BK == 32) return (row >> 2) & 3;
+  else return ((row >> 1) ^ (row >> 4)) & 7;
+}
+
+// A wave-uniform pointer held in scalar registers (buffer resources must be).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return reinterpret_cast<T*>(lo | (hi << 32));
+}
+
+// Operand tiles are read through one buffer resource per operand spanning the whole matrix: a load
+// at or past its last byte reads as zero, which is what rows past M (or N) and k-rows past K get.
+// Offsets are 32-bit (the host checks that they cannot wrap).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const uint16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(const_cast<uint16_t*>(base)), 0, (int)bytes, 0x00020000);
+}
+
+// Thread (wave w, lane l)'s kVecs 16-byte vectors of a 256 x BK operand tile:
+//   K-major ([row][K], ld bytes per row): vector i is tile row kInstrRows (w kVecs + i) + l / kRowVecs,
+//   LDS slot l % kRowVecs, i.e. global k vector (l % kRowVecs) ^ swz(row); the 64 lanes of vector i
+//   fill 1 KiB of LDS in lane order. A step moves 2 BK bytes along k.
+//   M/N-major ([K][row], BK 64): vector i is k = 8 (t / 32) + i, rows 8 (t % 32) .. + 7; a step moves
+//   BK k-rows.
+template <class C, bool KMAJOR>
+__device__ __forceinline__ int kmajor_row(int t, int i) {
+  return C::kInstrRows * ((t >> 6) * C::kVecs + i) + (t & 63) / C::kRowVecs;
+}
+template <class C, bool KMAJOR>
+__device__ __forceinline__ int kmajor_kvec(int t, int i) {
+  return ((t & 63) % C::kRowVecs) ^ swz<C::BK>(kmajor_row<C, KMAJOR>(t, i));
+}
+template <class C, bool KMAJOR>
+__device__ __forceinline__ void tile_offsets(uint32_t ld_bytes, int row0, int k0, int t, uint32_t (&off)[C::kVecs]) {
+#pragma unroll
+  for (int i = 0; i < C::kVecs; ++i) {
+    if constexpr (KMAJOR) {
+      off[i] = (uint32_t)(row0 + kmajor_row<C, KMAJOR>(t, i)) * ld_bytes + 2u * (uint32_t)k0 +
+               16u * (uint32_t)kmajor_kvec<C, KMAJOR>(t, i);
+    } else {
+      off[i] = (uint32_t)(k0 + 8 * (t / 32) + i) * ld_bytes + 2u * (uint32_t)(row0 + 8 * (t % 32));
+    }
+  }
+}
+template <class C, bool KMAJOR>
+__device__ __forceinline__ uint32_t step_bytes(uint32_t ld_bytes) {
+  return KMAJOR ? 2u * C::BK : (uint32_t)C::BK * ld_bytes;
+}
+
+// K-major tile straight into LDS: vector i of wave w lands at rows kInstrRows (w kVecs + i) ...
+template <int NV>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, const uint32_t* off, uint8_t* tile, int wave) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(tile + 1024 * (wave * NV + i)), 16, off[i], 0, 0, 0);
+}
+
+// Loads one operand tile into registers. MASKED (the last, partial K step only): k at or past kend
+// reads as zero; a K-major vector can straddle kend (K not a multiple of 8), and its elements past
+// kend, which may hold anything (row padding), are zeroed one by one.
+template <class C, bool KMAJOR, bool MASKED>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t r, const uint32_t (&off)[C::kVecs], int k0, int kend,
+                                          int t, u32x4 (&v)[C::kVecs]) {
+#pragma unroll
+  for (int i = 0; i < C::kVecs; ++i) {
+    u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off[i], 0, 0);
+    if constexpr (MASKED) {
+      if constexpr (KMAJOR) {
+        const int n = kend - (k0 + 8 * kmajor_kvec<C, KMAJOR>(t, i));  // valid elements (<= 0: none)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = 2 * e + 1 < n ? x[e] : 2 * e < n ? (x[e] & 0xffffu) : 0u;
+      } else {
+        if (k0 + 8 * (t / 32) + i >= kend) x = u32x4{0, 0, 0, 0};
+      }
+    }
+    v[i] = x;
+  }
+}
+
+// Writes the registers of load_tile to the (swizzled) LDS tile.
+template <class C, bool KMAJOR>
+__device__ __forceinline__ void store_tile(uint8_t* tile, int t, const u32x4 (&v)[C::kVecs]) {
+  if constexpr (KMAJOR) {  // the image the LDS-DMA loads would have written
+#pragma unroll
+    for (int i = 0; i < C::kVecs; ++i)
+      *reinterpret_cast<u32x4*>(tile + 1024 * ((t >> 6) * C::kVecs + i) + 16 * (t & 63)) = v[i];
+  } else {
+    // v[i] holds rows 8 g .. 8 g + 7 at k = 8 q + i (g = t % 32, q = t / 32); each of the 8 rows gets
+    // its 8 k values (k vector q) as one 16-byte write (byte permutes pick the rows' halves)
+    const int g = t % 32, q = t / 32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // rows 8 g + 2 j (low halves) and 8 g + 2 j + 1 (high halves)
+      u32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = __builtin_amdgcn_perm(v[2 * e + 1][j], v[2 * e][j], 0x05040100u);
+        hi[e] = __builtin_amdgcn_perm(v[2 * e + 1][j], v[2 * e][j], 0x07060302u);
+      }
+      const int r0 = 8 * g + 2 * j, r1 = r0 + 1;
+      *reinterpret_cast<u32x4*>(tile + r0 * C::kRowBytes + 16 * (q ^ swz<C::BK>(r0))) = lo;
+      *reinterpret_cast<u32x4*>(tile + r1 * C::kRowBytes + 16 * (q ^ swz<C::BK>(r1))) = hi;
+    }
+  }
+}
+
+// One wave's MFMA operands for one 16-wide k slice: 4 A fragments (rows of its 128-row half) and 4 B
+// fragments (columns of its 128-column half). Lane l holds row (or column) l % 32, k = 8 (l / 32) .. + 7.
+// arow / brow: byte offset of the lane's row in the wave's first fragment; slot: the 16-byte slot of the
+// slice's k vector in that row. Rows 32 i further on (the halves start at multiples of 128 rows, where
+// the swizzles vanish) are swizzled alike for 64-byte rows and by an extra 2 i for 128-byte rows.
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+template <class C>
+__device__ __forceinline__ void read_frags(const uint8_t* stage, uint32_t arow, uint32_t brow, uint32_t slot, Frags& f) {
+  constexpr uint32_t kX = C::BK == 64 ? 2 : 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const u32x4*>(stage + arow + 32 * i * C::kRowBytes + 16 * (slot ^ (kX * i))));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    f.b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + C::kTileBytes + brow + 32 * j * C::kRowBytes +
+                                                                           16 * (slot ^ (kX * j))));
+}
+// Half of the 16 products of one slice: A fragments 2 h and 2 h + 1.
+__device__ __forceinline__ void mfma_8(const Frags& f, f32x16 (&acc)[4][4], int h) {
+#pragma unroll
+  for (int i = 2 * h; i < 2 * h + 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_16(const Frags& f, f32x16 (&acc)[4][4]) {
+  mfma_8(f, acc, 0);
+  mfma_8(f, acc, 1);
+}
+
+// Row statistics of one 32 x 32 output block row-group over a lane's columns: see the epilogue.
+__device__ __forceinline__ float half_max(float v) {  // over the 32 lanes of a half wave (same l / 32)
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float((int)p[0]), __int_as_float((int)p[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+  v = v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v = v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v = v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+  v = v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float((int)p[0]) + __int_as_float((int)p[1]);
+}
+__device__ __forceinline__ int half_min(int v) {
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true));
+  const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return min((int)p[0], (int)p[1]);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 0xC07F;
+
+template <bool A_KMAJOR, bool B_KMAJOR, bool STATS, bool BETA>
+__global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
+  using C = Cfg<A_KMAJOR, B_KMAJOR>;
+  constexpr int BK = C::BK, NST = C::kStages, AHEAD = C::kAhead, NV = C::kVecs;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int t = (int)__builtin_amdgcn_workitem_id_x();
+  const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;  // this wave's 128 x 128 quarter of the tile
+
+  // Tile order: the M tiles of one N tile run on the same XCD (workgroups are dispatched to the XCDs
+  // round-robin), so that they share the N tile's operand block in that XCD's L2.
+  const int b = (int)__builtin_amdgcn_workgroup_id_x();
+  const int mt = P.m_tiles;
+  const int xcd = b % 8, s = b / 8;
+  const int n_tile = 8 * (s / mt) + xcd, m_tile = s % mt;
+  if (n_tile >= P.n_tiles) return;  // padding of the tile order (uniform per workgroup)
+  const int m0 = m_tile * BM, n0 = n_tile * BN;
+  const int kz = (int)__builtin_amdgcn_workgroup_id_y();
+  const int kbeg = kz * P.kslice, kend = min(P.K, kbeg + P.kslice);
+  const int nsteps = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const int nfull = (kend - kbeg) / BK;  // steps that need no masking
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const __amdgpu_buffer_rsrc_t rA = operand_rsrc(P.A, P.a_bytes);
+  const __amdgpu_buffer_rsrc_t rB = operand_rsrc(P.B, P.b_bytes);
+  const uint32_t ldA = 2u * (uint32_t)P.lda, ldB = 2u * (uint32_t)P.ldb;
+  uint32_t oa[NV], ob[NV];  // offsets of the next step to load
+  tile_offsets<C, A_KMAJOR>(ldA, m0, kbeg, t, oa);
+  tile_offsets<C, B_KMAJOR>(ldB, n0, kbeg, t, ob);
+  const uint32_t sa = step_bytes<C, A_KMAJOR>(ldA), sb = step_bytes<C, B_KMAJOR>(ldB);
+  u32x4 ra[NV], rb[NV];
+  auto advance = [&]() {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      oa[i] += sa;
+      ob[i] += sb;
+    }
+  };
+  auto stage_ptr = [&](int st) { return smem + (st % NST) * C::kStageBytes; };
+  // Issues the loads of full step `st` (LDS-DMA for K-major operands, registers otherwise) and moves
+  // the offsets on.
+  auto issue = [&](int st) {
+    uint8_t* sp = stage_ptr(st);
+    if constexpr (A_KMAJOR) dma_tile<NV>(rA, oa, sp, wave);
+    else load_tile<C, false, false>(rA, oa, 0, 0, t, ra);
+    if constexpr (B_KMAJOR) dma_tile<NV>(rB, ob, sp + C::kTileBytes, wave);
+    else load_tile<C, false, false>(rB, ob, 0, 0, t, rb);
+    advance();
+  };
+
+  // Fragment rows: row l % 32 of the wave's halves; slice q reads k vector 2 q + l / 32.
+  const int fr = lane & 31, fh = lane >> 5;
+  const uint32_t arow = (uint32_t)(wm * 128 + fr) * C::kRowBytes, brow = (uint32_t)(wn * 128 + fr) * C::kRowBytes;
+  uint32_t fs[C::kSlices];
+#pragma unroll
+  for (int q = 0; q < C::kSlices; ++q) fs[q] = (uint32_t)((2 * q + fh) ^ swz<BK>(fr));
+
+  // Each full step st: the loads of step st + AHEAD go out one per product of the first slice; the
+  // k slices of the step run from LDS with the fragments of slice + 1 read while slice's products run;
+  // register-held tiles are written to the next stage between the products of the slice before the
+  // last (so for BK 32 the register path is not used in full steps); the barrier (after the next stage's loads have landed) sits in the middle of the last
+  // slice's products, which cover it and the next step's first fragment reads.
+  Frags f0, f1;
+  auto first_fragments = [&](const uint8_t* stage) {
+    __builtin_amdgcn_s_waitcnt(0);  // every load so far (LDS-DMA included) has landed
+    __syncthreads();
+    read_frags<C>(stage, arow, brow, fs[0], f0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  };
+  auto step = [&](auto issue_c, auto next_c, int st) {
+    constexpr bool ISSUE = decltype(issue_c)::value;  // issue the loads of full step st + AHEAD
+    constexpr bool NEXT = decltype(next_c)::value;    // a full step st + 1 follows (its stage is ready)
+    const uint8_t* cur = stage_ptr(st);
+    uint8_t* nxt = stage_ptr(st + 1);
+    constexpr int kLoads = 2 * NV;
+    constexpr int kWrites = (A_KMAJOR ? 0 : NV) + (B_KMAJOR ? 0 : NV);
+    // fc: this slice's fragments; fn: the next slice's (or the next step's first)
+    auto slice = [&](auto qc, Frags& fc, Frags& fn) {
+      constexpr int q = decltype(qc)::value;
+      constexpr bool LAST = q == C::kSlices - 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!LAST) {
+        constexpr bool WRITE = q == C::kSlices - 2 && NEXT && kWrites > 0;  // register-held tiles out
+        read_frags<C>(cur, arow, brow, fs[q + 1], fn);
+        if constexpr (q == 0 && ISSUE) issue(st + AHEAD);
+        if constexpr (WRITE) {
+          if constexpr (!A_KMAJOR) store_tile<C, false>(nxt, t, ra);
+          if constexpr (!B_KMAJOR) store_tile<C, false>(nxt + C::kTileBytes, t, rb);
+        }
+        mfma_16(fc, acc);
+        if constexpr (q == 0 && ISSUE) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 fragment reads
+#pragma unroll
+          for (int u = 0; u < kLoads; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one load
+          }
+        }
+        if constexpr (WRITE) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 fragment reads
+#pragma unroll
+          for (int u = 0; u < kWrites; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one 16-byte LDS write
+          }
+        }
+      } else {
+        mfma_8(fc, acc, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NEXT) {
+          // The next step's loads have landed once at most those issued after them (steps st + 2 ..
+          // st + AHEAD, when this step issued) are still in flight.
+          if constexpr (ISSUE) __builtin_amdgcn_s_waitcnt(waitcnt_vm((AHEAD - 1) * (A_KMAJOR + B_KMAJOR) * NV));
+          else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+          __syncthreads();
+          read_frags<C>(nxt, arow, brow, fs[0], fn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_8(fc, acc, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    slice(std::integral_constant<int, 0>{}, f0, f1);
+    slice(std::integral_constant<int, 1>{}, f1, f0);
+    if constexpr (C::kSlices == 4) {
+      slice(std::integral_constant<int, 2>{}, f0, f1);
+      slice(std::integral_constant<int, 3>{}, f1, f0);
+    }
+    // The next step's first fragments (in f0: the slice count is even) have landed while these
+    // products were issued; waiting here keeps the next step's first products from waiting for reads
+    // issued ahead of them.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  };
+  static_assert(C::kSlices % 2 == 0, "slices alternate between two fragment sets");
+
+  // Steps: a partial one (K not a multiple of BK: the last k range, loaded through registers with
+  // masking) goes first, as step 0, so that every step runs through the same pipeline; the full steps
+  // follow in k order.
+  if (nsteps > 0) {
+    if (nfull < nsteps) {
+      uint32_t ta[NV], tb[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        ta[i] = oa[i] + (uint32_t)nfull * sa;
+        tb[i] = ob[i] + (uint32_t)nfull * sb;
+      }
+      const int k1 = kbeg + nfull * BK;
+      load_tile<C, A_KMAJOR, true>(rA, ta, k1, kend, t, ra);
+      load_tile<C, B_KMAJOR, true>(rB, tb, k1, kend, t, rb);
+      store_tile<C, A_KMAJOR>(stage_ptr(0), t, ra);
+      store_tile<C, B_KMAJOR>(stage_ptr(0) + C::kTileBytes, t, rb);
+    } else {
+      issue(0);
+      if constexpr (!A_KMAJOR) store_tile<C, false>(stage_ptr(0), t, ra);
+      if constexpr (!B_KMAJOR) store_tile<C, false>(stage_ptr(0) + C::kTileBytes, t, rb);
+    }
+#pragma unroll
+    for (int a = 1; a < AHEAD; ++a)  // (DMA configurations only)
+      if (a < nsteps) issue(a);
+    first_fragments(stage_ptr(0));
+    int st = 0;
+#pragma nounroll
+    for (; st + AHEAD < nsteps; ++st) step(std::true_type{}, std::true_type{}, st);
+    if constexpr (AHEAD > 1) {
+#pragma nounroll
+      for (; st + 1 < nsteps; ++st) step(std::false_type{}, std::true_type{}, st);
+    }
+    step(std::false_type{}, std::false_type{}, st);
+  }
+
+  // ---- write C (or this K slice's partial) and, for the logits, the row statistics
+  float* out = P.k_split > 1 ? P.partial + (int64_t)kz * P.M * (int64_t)P.ldc : P.C;
+  const int col = lane & 31, rq = 4 * (lane >> 5);
+  // Stores go through a buffer resource based at the tile's corner whose extent ends with the
+  // matrix's last row: rows past M are dropped by the range check, columns past N by the lane mask.
+  // Lane l holds column 32 j + l % 32 and rows 8 (r / 4) + 4 (l / 32) + r % 4 of block (i, j).
+  const int64_t corner = (int64_t)m0 * P.ldc + n0;
+  const int64_t remain = ((int64_t)P.M * P.ldc - corner) * 4;
+  const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(out + corner), 0, __builtin_amdgcn_readfirstlane((int)(remain < 0xFFFFFFFFll ? remain : 0xFFFFFFFFll)),
+      0x00020000);
+  const uint32_t ldc4 = 4u * (uint32_t)P.ldc;
+  const uint32_t lane_off = (uint32_t)(wm * 128 + rq) * ldc4 + 4u * (uint32_t)(wn * 128 + col);
+  bool nok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) nok[j] = n0 + wn * 128 + 32 * j + col < P.N;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (nok[j]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t off = lane_off + (uint32_t)(32 * i + 8 * (r / 4) + (r % 4)) * ldc4 + 128u * j;
+          float v = acc[i][j][r];
+          if constexpr (BETA) v += P.beta * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC, (int)off, 0, 0));
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rC, (int)off, 0, 0);
+        }
+    }
+  }
+  if constexpr (STATS) {
+    // Per row of this wave's quarter: max over its (valid) 128 columns, the lowest column holding it,
+    // and the sum of exp(c - max). Lanes l and l + 32 hold different rows; the 32 lanes of a half hold
+    // the 32 columns of a block, four blocks per lane.
+    float* st_base = P.stats + (2 * n_tile + wn) * 3;
+    const int64_t st_ld = 2 * P.n_tiles * 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = nok[j] ? acc[i][j][r] : -__builtin_inff();
+        const float mx = half_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+        int li = 0x7fffffff;  // lowest column (relative to the wave's half tile) holding the max
+        float ls = 0.f;
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (v[j] == mx) li = 32 * j + col;
+          ls += nok[j] ? __expf(v[j] - mx) : 0.f;
+        }
+        const int ix = half_min(li);
+        const float sm = half_sum(ls);
+        const int m = m0 + wm * 128 + 32 * i + 8 * (r / 4) + rq + (r % 4);
+        if (col == 0 && m < P.M) {
+          float* stp = st_base + (int64_t)m * st_ld;
+          stp[0] = mx;
+          stp[1] = __int_as_float(ix + n0 + wn * 128);
+          stp[2] = sm;
+        }
+      }
+    }
+  }
+}
+
+// Sums the K slices of a split product in slice order: C = sum_z partial[z] (+ beta C).
+__global__ void __launch_bounds__(256) k_splitk_reduce(const float* partial, float* C, int64_t ldc, int M, int N,
+                                                       int k_split, float beta) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t m = i / N, n = i % N;
+    float s = 0.f;
+    for (int z = 0; z < k_split; ++z) s += partial[(int64_t)z * M * ldc + m * ldc + n];
+    float* c = C + m * ldc + n;
+    *c = beta != 0.f ? s + beta * *c : s;
+  }
+}
+
+// Per-row logits statistics from the product's half-tile partials, combined in column order:
+// max, lowest index of the max, log-sum-exp. One wave per row. maxlse [M][2] = (max, LSE) and arg [M]
+// may each be NULL.
+__global__ void __launch_bounds__(256) k_zstats_reduce(const float* part, int n_parts, int M, float* maxlse,
+                                                       int32_t* arg) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const float* p = part + (int64_t)m * n_parts * 3;
+  float mx = -__builtin_inff();
+  for (int q = lane; q < n_parts; q += 64) mx = fmaxf(mx, p[3 * q]);
+  for (int o = 32; o; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  int ix = 0x7fffffff;
+  float s = 0.f;
+  for (int q = lane; q < n_parts; q += 64) {
+    const float pm = p[3 * q];
+    if (pm == mx) ix = min(ix, __float_as_int(p[3 * q + 1]));
+    if (pm > -__builtin_inff()) s += p[3 * q + 2] * __expf(pm - mx);
+  }
+  for (int o = 32; o; o >>= 1) {
+    ix = min(ix, __shfl_xor(ix, o));
+    s += __shfl_xor(s, o);
+  }
+  if (lane == 0) {
+    if (maxlse) {
+      maxlse[2 * m] = mx;
+      maxlse[2 * m + 1] = mx + __logf(s);
+    }
+    if (arg) arg[m] = ix;
+  }
+}
+
+typedef void (*GemmKernel)(GemmParams);
+
+template <bool AK, bool BK_, bool S, bool B>
+GemmKernel kernel_of() {
+  return k_gemm<AK, BK_, S, B>;
+}
+
+}  // namespace
+
+size_t gemm_lds_bytes() { return kLdsBytes; }
+
+hipError_t launch_gemm(GemmParams p, bool a_kmajor, bool b_kmajor, hipStream_t s) {
+  p.m_tiles = (p.M + BM - 1) / BM;
+  p.n_tiles = (p.N + BN - 1) / BN;
+  if (p.k_split < 1) p.k_split = 1;
+  p.kslice = ((p.K + p.k_split - 1) / p.k_split + 63) / 64 * 64;  // a multiple of either K step
+  const bool beta = p.k_split == 1 && p.beta != 0.f;  // split products apply beta in the reduction
+  GemmKernel k = nullptr;
+  if (a_kmajor && b_kmajor && !beta) k = p.stats ? kernel_of<true, true, true, false>() : kernel_of<true, true, false, false>();
+  else if (a_kmajor && !b_kmajor && !p.stats) k = beta ? kernel_of<true, false, false, true>() : kernel_of<true, false, false, false>();
+  else if (!a_kmajor && !b_kmajor && !p.stats) k = beta ? kernel_of<false, false, false, true>() : kernel_of<false, false, false, false>();
+  if (!k) return hipErrorInvalidValue;
+  // more than 64 KiB of dynamic LDS (set on every launch: the setting is per device)
+  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e != hipSuccess) return e;
+  const int grid = 8 * p.m_tiles * ((p.n_tiles + 7) / 8);
+  void* args[] = {&p};
+  e = hipLaunchKernel((const void*)k, dim3(grid, p.k_split), dim3(kGemmThreads), args, kLdsBytes, s);
+  if (e != hipSuccess) return e;
+  if (p.k_split > 1) {
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(1024), dim3(256), 0, s, p.partial, p.C, p.ldc, p.M, p.N, p.k_split, p.beta);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_zstats_reduce(const float* part, int n_parts, int M, float* maxlse, int32_t* arg, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zstats_reduce, dim3((M + 3) / 4), dim3(256), 0, s, part, n_parts, M, maxlse, arg);
+  return hipGetLastError();
+}
+
+}  // namespace opd

@@ -1,16 +1,12 @@
-// Plain dense products of the lm_head-fused path through rocBLAS: bf16 operands, fp32 accumulation
-// and output. These three GEMMs (logits = h W^T, dh = dz W, dW = dz^T h) are ordinary library
-// matrix products on the MFMA units; the loss, its gradient and the top-1s between them run in the
-// library's own row-team kernel.
-//
-// One rocBLAS handle per device, created on first use and kept for the life of the process (rocBLAS
-// allocates its own device workspace inside it). Atomics are disabled on the handle so that every
-// product is reproduced bit for bit. Calls serialise on a mutex while they set the handle's stream
-// and enqueue.
+// Host side of the lm_head-fused path's matrix products: argument checks and launch planning for the
+// library's own bf16 MFMA kernels (opd_gemm.hip). The three products of a chunk of rows are
+//   logits  z  = h W^T       (M rows, N vocab, K hidden; both operands K-major)
+//   dh         = dz W        (M rows, N hidden, K vocab; dz K-major, W N-major; split over K)
+//   dW        (+)= dz^T h    (M vocab, N hidden, K rows; both operands M/N-major)
+// that the OPD loss of "AdaFlash: Adaptive Speculative Decoding with Online Self-Improvement for
+// High-Concurrency LLM Inference", section "1. On-Policy Distillation (OPD) for Domain Adaptation",
+// needs when the drafter's vocabulary projection is trained with it.
 
-#include <rocblas/rocblas.h>
-
-#include <mutex>
 #include <string>
 
 #include "opd_internal.h"
@@ -18,42 +14,56 @@
 namespace opd {
 namespace {
 
-std::mutex g_blas_mu;
-rocblas_handle g_blas[64] = {};
+constexpr int64_t kTile = kGemmTile;  // rows (or columns) of one workgroup tile
+constexpr int64_t kKStep = 64;        // K step of the kernels (and granule of a K slice)
 
-const char* blas_text(rocblas_status s) { return rocblas_status_to_string(s); }
+int64_t round_up64(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Largest byte offset the kernel can form for an operand (including the rows or k-rows that a last
+// tile or step reaches past the matrix, which read as zero); buffer offsets are 32-bit.
+bool offsets_fit(bool kmajor, int64_t rows, int64_t K, int64_t ld) {
+  const int64_t reach = kmajor ? round_up64(rows, kTile) + kTile : round_up64(K, kKStep) + kKStep;
+  return reach * ld * 2 < (int64_t)UINT32_MAX;
+}
 
 }  // namespace
 
-opd_status_t gemm_bf16_f32(bool trans_a, bool trans_b, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
-                           const void* B, int64_t ldb, float beta, float* C, int64_t ldc, hipStream_t stream) {
-  if (m <= 0 || n <= 0) return OPD_OK;
-  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX || lda > INT32_MAX || ldb > INT32_MAX || ldc > INT32_MAX)
+opd_status_t gemm_bf16_f32(const uint16_t* A, int64_t lda, bool a_kmajor, const uint16_t* B, int64_t ldb,
+                           bool b_kmajor, int64_t M, int64_t N, int64_t K, float beta, float* C, int64_t ldc,
+                           int k_split, float* partial, float* stats, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return OPD_OK;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || K < 0)
     return record_error(OPD_ERR_SHAPE, "matrix product dimensions exceed 32-bit sizes");
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-    return record_error(OPD_ERR_HIP, "hipGetDevice failed for the matrix product");
-  std::lock_guard<std::mutex> lk(g_blas_mu);
-  rocblas_handle& h = g_blas[dev];
-  if (!h) {
-    rocblas_status s = rocblas_create_handle(&h);
-    if (s != rocblas_status_success) {
-      h = nullptr;
-      return record_error(OPD_ERR_HIP, (std::string("rocblas_create_handle: ") + blas_text(s)).c_str());
-    }
-    rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed);
-  }
-  rocblas_status s = rocblas_set_stream(h, stream);
-  if (s != rocblas_status_success)
-    return record_error(OPD_ERR_HIP, (std::string("rocblas_set_stream: ") + blas_text(s)).c_str());
-  const float alpha = 1.f;
-  s = rocblas_gemm_ex(h, trans_a ? rocblas_operation_transpose : rocblas_operation_none,
-                      trans_b ? rocblas_operation_transpose : rocblas_operation_none, (rocblas_int)m, (rocblas_int)n,
-                      (rocblas_int)k, &alpha, A, rocblas_datatype_bf16_r, (rocblas_int)lda, B, rocblas_datatype_bf16_r,
-                      (rocblas_int)ldb, &beta, C, rocblas_datatype_f32_r, (rocblas_int)ldc, C, rocblas_datatype_f32_r,
-                      (rocblas_int)ldc, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  if (s != rocblas_status_success)
-    return record_error(OPD_ERR_HIP, (std::string("rocblas_gemm_ex: ") + blas_text(s)).c_str());
+  if ((a_kmajor && lda < K) || (!a_kmajor && lda < M) || (b_kmajor && ldb < K) || (!b_kmajor && ldb < N) || ldc < N)
+    return record_error(OPD_ERR_SHAPE, "matrix product leading dimension smaller than the matrix");
+  if (lda % 8 || ldb % 8) return record_error(OPD_ERR_ALIGN, "bf16 operand pitches must be multiples of 8");
+  if (!offsets_fit(a_kmajor, M, K, lda) || !offsets_fit(b_kmajor, N, K, ldb))
+    return record_error(OPD_ERR_SHAPE, "an operand of the matrix product spans 4 GiB or more (32-bit buffer offsets)");
+  if (kTile * ldc * 4 >= (int64_t)UINT32_MAX)
+    return record_error(OPD_ERR_SHAPE, "output pitch too large for 32-bit offsets within a tile");
+  if (k_split < 1) k_split = 1;
+  if (k_split > 1 && !partial) return record_error(OPD_ERR_WORKSPACE, "split product without partial buffer");
+  if (stats && (!a_kmajor || !b_kmajor || k_split > 1 || beta != 0.f))
+    return record_error(OPD_ERR_PARAM, "row statistics only for the unsplit logits product");
+  GemmParams p{};
+  p.A = A;
+  p.lda = lda;
+  p.a_bytes = (uint32_t)((a_kmajor ? M : K) * lda * 2);
+  p.B = B;
+  p.ldb = ldb;
+  p.b_bytes = (uint32_t)((b_kmajor ? N : K) * ldb * 2);
+  p.C = C;
+  p.ldc = ldc;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.beta = beta;
+  p.k_split = k_split;
+  p.partial = partial;
+  p.stats = stats;
+  hipError_t e = launch_gemm(p, a_kmajor, b_kmajor, stream);
+  if (e != hipSuccess)
+    return record_error(OPD_ERR_HIP, (std::string("matrix product launch: ") + hipGetErrorString(e)).c_str());
   return OPD_OK;
 }
 

@@ -237,9 +237,11 @@ opd_status_t opd_verify_sample(const void* z, const void* y, opd_dtype_t dt, int
  * the drafter is what the online update trains); the pages show neither the drafter's head nor its
  * sizes, so h is read as the drafter's final hidden states and W as its projection (no bias), and
  * the gradient flows to both. Rows are processed in chunks of chunk_rows: per chunk, z (fp32) =
- * h W^T into scratch (rocBLAS, bf16 operands, fp32 accumulation), the fused loss / gradient / top-1
- * pass of opd_fused_fwd_bwd_verify over that chunk (dz as bf16 into scratch), dh = dz W and
- * dW (+)= dz^T h (rocBLAS); then the accept lengths of all blocks.
+ * h W^T into scratch, the fused loss / gradient / top-1 pass of opd_fused_fwd_bwd_verify over that
+ * chunk (dz as bf16 into scratch), dh = dz W and dW (+)= dz^T h; then the accept lengths of all
+ * blocks. The three products run on the library's own bf16 MFMA kernels (fp32 accumulation and
+ * output); the logits product also forms each row's max, lowest argmax and log-sum-exp in its
+ * epilogue.
  *   h          [n_rows, hidden] bf16, row-major, pitch hidden (hidden a multiple of 8).
  *   W          [vocab, hidden] bf16, row-major, pitch hidden.
  *   y          [n_rows, ld_y] target logits, dt_y must be OPD_F32 (the logits chunk is fp32 and the
@@ -248,14 +250,19 @@ opd_status_t opd_verify_sample(const void* z, const void* y, opd_dtype_t dt, int
  *              may be NULL only without blocks); grad_loss [n_rows] or NULL.
  *   dh         [n_rows, hidden] f32 out (overwritten), or NULL to skip.
  *   dW         [vocab, hidden] f32 out (overwritten: the sum over all chunks), or NULL to skip.
+ *   logit_max_lse [n_rows][2] f32 out (max z, log sum_v e^z_v) from the product's epilogue, or NULL.
+ *   logit_argmax  [n_rows] int32 out (lowest index of max z) from the same epilogue, or NULL. With
+ *              both NULL the epilogue statistics are skipped.
  *   scratch    caller device memory of at least opd_lmhead_scratch_size(min(chunk_rows, n_rows),
- *              vocab, ld_y) bytes, 16-byte aligned: one chunk of fp32 logits and of bf16 dz.
- * dh and dW are formed from the bf16-rounded dz of the row kernel. The three products go through
- * rocBLAS, which keeps one handle (and its own device workspace) per device for the process,
- * created (with a device allocation) on the first call on a device; the handle has atomics
- * disabled, so results are deterministic. This call is not tested under stream capture.
- * Errors: OPD_ERR_NULL, OPD_ERR_SHAPE, OPD_ERR_DTYPE (dt_y not OPD_F32), OPD_ERR_ALIGN,
- * OPD_ERR_PARAM, OPD_ERR_WORKSPACE (ws or scratch too small), OPD_ERR_HIP (including rocBLAS errors).
+ *              vocab, ld_y) bytes, 16-byte aligned: one chunk of fp32 logits (which later holds the
+ *              dh product's split-K partials) and of bf16 dz (which first holds the logits
+ *              statistics partials).
+ * dh and dW are formed from the bf16-rounded dz of the row kernel. Size limits of the products:
+ * every operand (W: vocab x hidden x 2 bytes; a chunk of h or dz) under 4 GiB, and 256 rows of the
+ * logits chunk under 4 GiB (32-bit buffer offsets). Nothing is allocated. This call is not tested
+ * under stream capture.
+ * Errors: OPD_ERR_NULL, OPD_ERR_SHAPE (including the size limits), OPD_ERR_DTYPE (dt_y not OPD_F32),
+ * OPD_ERR_ALIGN, OPD_ERR_PARAM, OPD_ERR_WORKSPACE (ws or scratch too small), OPD_ERR_HIP.
  */
 size_t opd_lmhead_scratch_size(int64_t chunk_rows, int64_t vocab, int64_t ld_y);
 opd_status_t opd_lmhead_fused_fwd_bwd_verify(const void* h, const void* W, int64_t hidden, const void* y,
@@ -263,8 +270,9 @@ opd_status_t opd_lmhead_fused_fwd_bwd_verify(const void* h, const void* W, int64
                                              const opd_blocks_t* blocks, float alpha, float tau,
                                              const float* grad_loss, float* loss, int32_t* target_top1,
                                              int32_t* draft_top1, float* row_stats, float* dh, float* dW,
-                                             int32_t* accept_len, void* scratch, size_t scratch_bytes,
-                                             int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream);
+                                             float* logit_max_lse, int32_t* logit_argmax, int32_t* accept_len,
+                                             void* scratch, size_t scratch_bytes, int64_t chunk_rows, void* ws,
+                                             size_t ws_bytes, hipStream_t stream);
 
 /*
  * Host-side batch scheduling ("AdaFlash: Adaptive Speculative Decoding with Online Self-Improvement

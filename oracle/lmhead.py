@@ -19,10 +19,14 @@ Readings (the pages show neither the drafter's head nor its sizes):
 * the gradient flows to both h and W: dh = dz W, dW = dz^T h, with dz = w_r * d loss_r / d z_r;
   y (the target's logits) takes no gradient.
 
+* the per-row statistics of z that the logits product reports (max, lowest index of the max,
+  log-sum-exp) are their plain definitions.
+
 Each step is a library primitive (a matmul) or a function of ``oracle/opd_oracle.py``, whose pins
 hold for it. Pinned by ``tests/test_lmhead_pins.py``: central finite differences of
-sum_r w_r loss_r with respect to h and W, and the special case W = I (then z = h and dh = dz).
-No function here is parity-unpinned.
+sum_r w_r loss_r with respect to h and W, the special case W = I (then z = h and dh = dz), and for
+``logit_stats`` constant rows (LSE = c + log V, argmax 0), a two-level row in closed form and an
+exact rational-sum check on small rows. No function here is parity-unpinned.
 """
 
 from __future__ import annotations
@@ -31,7 +35,7 @@ import numpy as np
 
 from oracle import opd_oracle as O
 
-__all__ = ["lmhead_rows", "lmhead_fused"]
+__all__ = ["lmhead_rows", "lmhead_fused", "logit_stats"]
 
 
 def lmhead_rows(h, W, rows) -> np.ndarray:
@@ -41,11 +45,21 @@ def lmhead_rows(h, W, rows) -> np.ndarray:
     return h[np.asarray(rows)] @ W.T
 
 
+def logit_stats(z):
+    """Per row of z: (max, lowest index holding the max, log sum_v exp z_v), in float64."""
+    z = np.asarray(z, dtype=np.float64)
+    mx = z.max(axis=1)
+    arg = np.argmax(z, axis=1)  # the first (lowest) index of the maximum
+    lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=1))
+    return mx, arg.astype(np.int64), lse
+
+
 def lmhead_fused(h, W, y, alpha: float, tau: float, offsets=None, lengths=None, grad_loss=None) -> dict:
     """Loss, top-1s, accept lengths and the gradients w.r.t. h and W of the lm_head-fused path.
 
     h [R, H], W [V, H], y [R, V] (exact values of the device inputs). Returns z, loss, dz, dh, dW,
-    S, target_top1, draft_top1 and (with offsets and lengths) accept_len and flags.
+    S, target_top1, draft_top1, logit_max, logit_argmax, logit_lse and (with offsets and lengths)
+    accept_len and flags.
     """
     h = np.asarray(h, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
@@ -63,6 +77,7 @@ def lmhead_fused(h, W, y, alpha: float, tau: float, offsets=None, lengths=None, 
         "target_top1": fwd["target_top1"],
         "draft_top1": fwd["draft_top1"],
     }
+    out["logit_max"], out["logit_argmax"], out["logit_lse"] = logit_stats(z)
     if offsets is not None:
         out["accept_len"], out["flags"] = O.accept_lengths(fwd["draft_top1"], fwd["target_top1"], offsets, lengths)
     return out

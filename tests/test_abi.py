@@ -135,7 +135,7 @@ def test_lmhead_validation(lib):
              dW=P, scratch=P, scb=sc, rc=16, wsp=WS, wsb=ws, blocks=None):
         b = ctypes.byref(blocks) if blocks is not None else None
         return lib.opd_lmhead_fused_fwd_bwd_verify(h, W, H, y, dt, n, v, ld, b, a, t, None, loss, top, dtop, st, dh,
-                                                   dW, None, scratch, scb, rc, wsp, wsb, None)
+                                                   dW, None, None, None, scratch, scb, rc, wsp, wsb, None)
 
     # (a call that passes validation would launch kernels on the fake pointers: never made here)
     assert call(dt=BF16) == 3

@@ -1,7 +1,11 @@
 """GPU parity of the lm_head-fused path (opd_lmhead_fused_fwd_bwd_verify) against the float64 oracle.
 
 The oracle forms z = h W^T in float64 from the exact bf16 inputs; the GPU forms it with fp32
-accumulation (rocBLAS) and runs the row kernel on it, then dh and dW from the bf16-rounded dz.
+accumulation (the library's MFMA product kernels) and runs the row kernel on it, then dh and dW from
+the bf16-rounded dz. The logits product's epilogue statistics (max, lowest argmax, log-sum-exp per
+row) are checked against the oracle's definitions (the max and LSE within the fp32-logits bound used
+for the row kernel's LSE, the argmax like the draft top-1) and against the row kernel's own draft
+top-1 and LSE(z) on the same fp32 logits (the argmax exactly).
 Bounds used (per element of dh and dW): the row kernel's dz tolerance (2e-5 absolute) plus the bf16
 rounding of dz (a relative 2^-9, allowed as 2^-8) carried through the product with |W| or |h|; the
 fp32 accumulation of the products is far below that. The loss within 1e-3 relative + 3e-5 (the
@@ -10,7 +14,9 @@ top-1 exactly except where two logits are within 1e-4 (fp32 accumulation may ord
 way). Inputs avoid reverse-KL terms within 1e-3 tau of the clip point, where a term may land on
 either side.
 
-Sizes: a few chunks with a ragged last chunk at V = 1000 and 1003, H = 64 / 72; the full vocabulary
+Sizes: a few chunks with a ragged last chunk at V = 1000 and 1003, H = 64 / 72 (K steps with a
+partial last step in all three products, and dz rows whose bf16 padding the dh product must mask),
+one single-row call; the full vocabulary
 151,936 with H = 4096 over 64 rows in three chunks (every output compared); and the benchmark's
 configuration (2048 rows, one chunk) on sampled rows.
 """
@@ -114,13 +120,33 @@ def _run_and_check_all(lib, seed, R, V, H, ld, chunk, wscale, alpha, tau, blocks
     assert np.all(err <= tol_dW), f"dW: worst excess {np.max(err - tol_dW):.3g}"
     # the bound is not vacuous: the typical error sits far below it
     assert np.median(np.abs(g["dh"] - ref["dh"])) < 0.1 * np.median(tol_dh)
+    _check_logit_stats(g, ref["logit_max"], ref["logit_lse"], ref["z"], range(R))
 
 
-@pytest.mark.parametrize("seed,R,V,H,ld,chunk", [(1, 40, 1000, 64, 1000, 16), (2, 37, 1003, 72, 1008, 10)])
+def _check_logit_stats(g, mx_ref, lse_ref, z_ref, rows):
+    rows = list(rows)
+    ml = g["logit_max_lse"][rows]
+    assert np.all(np.abs(ml[:, 0] - mx_ref) <= 2e-5 * (1 + np.abs(mx_ref)))
+    assert np.all(np.abs(ml[:, 1] - lse_ref) <= 2e-5 * (1 + np.abs(lse_ref)))
+    _check_draft_top1(z_ref, g["logit_argmax"], rows)
+    # the same fp32 logits as the row kernel's: the same lowest argmax, and LSE(z) to fp32 rounding
+    assert np.array_equal(g["logit_argmax"][rows], g["draft_top1"][rows])
+    lse_team = g["row_stats"][rows, 0]
+    assert np.all(np.abs(ml[:, 1] - lse_team) <= 2e-6 * (1 + np.abs(lse_team)))
+
+
+@pytest.mark.parametrize("seed,R,V,H,ld,chunk", [(1, 40, 1000, 64, 1000, 16), (2, 37, 1003, 72, 1008, 10),
+                                                 (12, 300, 2053, 136, 2056, 300)])
 def test_lmhead_small_chunks(lib, seed, R, V, H, ld, chunk):
     off = np.array([0, 16, 20, 20, R], dtype=np.int32)
     L = np.array([16, 3, 0, 9], dtype=np.int32)
     _run_and_check_all(lib, seed, R, V, H, ld, chunk, 0.35, 0.6, 0.05, (off, L))
+
+
+def test_lmhead_single_row(lib):
+    off = np.array([0, 1], dtype=np.int32)
+    L = np.array([1], dtype=np.int32)
+    _run_and_check_all(lib, 8, 1, 777, 40, 780, 5, 0.35, 0.6, 0.05, (off, L))
 
 
 def test_lmhead_full_vocab_hidden_4096(lib):
@@ -169,9 +195,15 @@ def test_lmhead_benchmark_configuration_sampled_rows(lib):
         ref = dz @ W
         tol = (2e-5 + 2.0 ** -8 * np.abs(dz)) @ np.abs(W) + 1e-6
         assert np.all(np.abs(dh[r] - ref) <= tol), f"row {r}"
+    g = {k: out[k].cpu().numpy() for k in ("logit_max_lse", "logit_argmax", "draft_top1", "row_stats")}
+    mx, _, lse = LM.logit_stats(z_rows)
+    _check_logit_stats(g, mx, lse, z_rows, rows)
+    # over every row: the epilogue's argmax is the row kernel's draft top-1, its LSE the kernel's LSE(z)
+    assert np.array_equal(g["logit_argmax"], g["draft_top1"])
+    assert np.all(np.abs(g["logit_max_lse"][:, 1] - g["row_stats"][:, 0]) <= 2e-6 * (1 + np.abs(g["row_stats"][:, 0])))
     out2 = lib.lmhead_fused_fwd_bwd_verify(ht, Wt, yt, off, L, 0.5, 0.05, chunk_rows=2048)
     torch.cuda.synchronize()
-    for k in ("loss", "dh", "dW", "accept_len"):
+    for k in ("loss", "dh", "dW", "accept_len", "logit_max_lse", "logit_argmax"):
         assert torch.equal(out[k], out2[k]), k
 
 
@@ -189,8 +221,13 @@ def test_lmhead_optional_outputs_and_empty_batch(lib):
     torch.cuda.synchronize()
     assert lib.read_flags(clear=True) == 0
     assert part["dh"] is None and part["dW"] is None
-    for k in ("loss", "target_top1", "draft_top1", "row_stats", "accept_len"):
+    for k in ("loss", "target_top1", "draft_top1", "row_stats", "accept_len", "logit_max_lse", "logit_argmax"):
         assert torch.equal(full[k], part[k]), k
+    nost = lib.lmhead_fused_fwd_bwd_verify(ht, Wt, yt, off, L, 0.5, 0.05, chunk_rows=7, want_logit_stats=False)
+    torch.cuda.synchronize()
+    assert nost["logit_max_lse"] is None and nost["logit_argmax"] is None
+    for k in ("loss", "target_top1", "draft_top1", "row_stats", "accept_len", "dh", "dW"):
+        assert torch.equal(full[k], nost[k]), k
     # grad_loss = 0 on every row: zero gradients
     zero = lib.lmhead_fused_fwd_bwd_verify(ht, Wt, yt, off, L, 0.5, 0.05, chunk_rows=7,
                                            grad_loss=torch.zeros(20, dtype=torch.float32, device="cuda"))

@@ -62,3 +62,34 @@ def test_identity_projection_reduces_to_the_logit_gradient():
     assert np.allclose(out["dh"], dz, rtol=0, atol=1e-15)
     assert np.allclose(out["dW"], dz.T @ h, rtol=0, atol=1e-15)
     assert np.array_equal(out["draft_top1"], np.argmax(h, axis=1))
+
+
+def test_logit_stats_constant_rows():
+    # every logit equal: max c, LSE c + log V, and the lowest index of the (tied) maximum is 0
+    for V, c in ((1, 0.25), (7, -3.0), (151936, 12.5)):
+        mx, arg, lse = LM.logit_stats(np.full((2, V), c))
+        assert np.all(mx == c) and np.all(arg == 0)
+        assert np.allclose(lse, c + np.log(V), rtol=0, atol=1e-12)
+
+
+def test_logit_stats_two_level_row_closed_form():
+    # k entries at a, the rest at b < a: LSE = a + log(k + (V - k) e^(b - a)); argmax = first a
+    V, k, a, b = 1000, 3, 2.0, -1.5
+    z = np.full(V, b)
+    pos = [17, 400, 999]
+    z[pos] = a
+    mx, arg, lse = LM.logit_stats(z[None, :])
+    assert mx[0] == a and arg[0] == 17
+    assert abs(lse[0] - (a + np.log(k + (V - k) * np.exp(b - a)))) < 1e-12
+
+
+def test_logit_stats_match_an_exact_sum():
+    # small rows: e^z summed with math.fsum from the definition, no shift
+    import math
+
+    rng = np.random.default_rng(11)
+    z = rng.normal(0, 3, (5, 37))
+    mx, arg, lse = LM.logit_stats(z)
+    for r in range(5):
+        assert mx[r] == max(z[r]) and arg[r] == list(z[r]).index(max(z[r]))
+        assert abs(lse[r] - math.log(math.fsum(math.exp(v) for v in z[r]))) < 1e-12
