@@ -41,19 +41,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256;
 constexpr int kGemmThreads = 256;
-constexpr int kLdsBytes = 128 * 1024;  // either configuration: 4 x 32 KiB or 2 x 64 KiB
+constexpr int kLdsBytes = 128 * 1024;  // two stages of 64 KiB
 
-// K step of the products with both operands K-major: 64 with two stages measured faster on the logits
-// product (2048 x 151936 x 4096) than 32 with a ring of four (2.6 vs 3.1 ms); both are supported.
-constexpr int kBothKmajorStep = 64;
-
-// Pipeline shape of a product: K step, stages in the LDS ring, and the derived sizes.
+// Pipeline shape of a product and the derived sizes (one shape for all products: K step 64, two LDS
+// stages; a ring of four 32-wide stages for the both-K-major product measured slower, 3.1 against
+// 2.6 ms on the 2048 x 151936 x 4096 logits product).
 template <bool A_KMAJOR, bool B_KMAJOR>
 struct Cfg {
-  static constexpr bool kDmaBoth = A_KMAJOR && B_KMAJOR;
-  static constexpr int BK = kDmaBoth ? kBothKmajorStep : 64;
-  static constexpr int kStages = kDmaBoth && BK == 32 ? 4 : 2;
-  static constexpr int kAhead = kStages - 1;             // steps loaded ahead
+  static constexpr int BK = 64;
+  static constexpr int kStages = 2;
   static constexpr int kRowBytes = 2 * BK;               // one LDS tile row
   static constexpr int kTileBytes = 256 * kRowBytes;     // one operand tile
   static constexpr int kStageBytes = 2 * kTileBytes;     // A and B
@@ -62,7 +58,6 @@ struct Cfg {
   static constexpr int kRowVecs = BK / 8;                // 16-byte vectors per tile row
   static constexpr int kInstrRows = 1024 / kRowBytes;    // tile rows one LDS-DMA instruction fills
   static_assert(kStages * kStageBytes == kLdsBytes, "LDS ring size");
-  static_assert(kDmaBoth || BK == 64, "register-held (transposed) tiles assume a K step of 64");
 };
 
 // LDS position of k vector kv of tile row `row`: 16-byte slot kv ^ swz(row). The LDS serves 16 lanes'
@@ -246,7 +241,7 @@ constexpr int kWaitLgkm0 = 0xC07F;
 template <bool A_KMAJOR, bool B_KMAJOR, bool STATS, bool BETA>
 __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
   using C = Cfg<A_KMAJOR, B_KMAJOR>;
-  constexpr int BK = C::BK, NST = C::kStages, AHEAD = C::kAhead, NV = C::kVecs;
+  constexpr int BK = C::BK, NST = C::kStages, NV = C::kVecs;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int t = (int)__builtin_amdgcn_workitem_id_x();
   const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -279,23 +274,20 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
   tile_offsets<C, B_KMAJOR>(ldB, n0, kbeg, t, ob);
   const uint32_t sa = step_bytes<C, A_KMAJOR>(ldA), sb = step_bytes<C, B_KMAJOR>(ldB);
   u32x4 ra[NV], rb[NV];
-  auto advance = [&]() {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      oa[i] += sa;
-      ob[i] += sb;
-    }
-  };
   auto stage_ptr = [&](int st) { return smem + (st % NST) * C::kStageBytes; };
-  // Issues the loads of full step `st` (LDS-DMA for K-major operands, registers otherwise) and moves
-  // the offsets on.
-  auto issue = [&](int st) {
-    uint8_t* sp = stage_ptr(st);
-    if constexpr (A_KMAJOR) dma_tile<NV>(rA, oa, sp, wave);
+  // Issues the loads of one operand of full step `st` (LDS-DMA for a K-major operand, registers
+  // otherwise) and moves its offsets on.
+  auto issue_a = [&](int st) {
+    if constexpr (A_KMAJOR) dma_tile<NV>(rA, oa, stage_ptr(st), wave);
     else load_tile<C, false, false>(rA, oa, 0, 0, t, ra);
-    if constexpr (B_KMAJOR) dma_tile<NV>(rB, ob, sp + C::kTileBytes, wave);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) oa[i] += sa;
+  };
+  auto issue_b = [&](int st) {
+    if constexpr (B_KMAJOR) dma_tile<NV>(rB, ob, stage_ptr(st) + C::kTileBytes, wave);
     else load_tile<C, false, false>(rB, ob, 0, 0, t, rb);
-    advance();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) ob[i] += sb;
   };
 
   // Fragment rows: row l % 32 of the wave's halves; slice q reads k vector 2 q + l / 32.
@@ -305,11 +297,16 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
 #pragma unroll
   for (int q = 0; q < C::kSlices; ++q) fs[q] = (uint32_t)((2 * q + fh) ^ swz<BK>(fr));
 
-  // Each full step st: the loads of step st + AHEAD go out one per product of the first slice; the
-  // k slices of the step run from LDS with the fragments of slice + 1 read while slice's products run;
-  // register-held tiles are written to the next stage between the products of the slice before the
-  // last (so for BK 32 the register path is not used in full steps); the barrier (after the next stage's loads have landed) sits in the middle of the last
-  // slice's products, which cover it and the next step's first fragment reads.
+  // Step st computes from stage st % 2 (cur) while the next step's tiles arrive in the other (nxt):
+  //   - an LDS-DMA A tile (K-major A) is issued two steps ahead, right after the barrier of the step
+  //     before, into the stage that barrier has just freed (one load per product of the second half
+  //     of the last slice);
+  //   - the B tile (LDS-DMA or registers) and a register-held A tile are issued in the first slice,
+  //     one load per product or two;
+  //   - register-held tiles are written to nxt between the third slice's products;
+  //   - the k slices run from LDS with the fragments of slice + 1 read while slice's products run;
+  //   - the barrier (after every load of nxt has landed) sits in the middle of the last slice, whose
+  //     products around it cover the barrier and the next step's first fragment reads.
   Frags f0, f1;
   auto first_fragments = [&](const uint8_t* stage) {
     __builtin_amdgcn_s_waitcnt(0);  // every load so far (LDS-DMA included) has landed
@@ -317,33 +314,37 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
     read_frags<C>(stage, arow, brow, fs[0], f0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   };
-  auto step = [&](auto issue_c, auto next_c, int st) {
-    constexpr bool ISSUE = decltype(issue_c)::value;  // issue the loads of full step st + AHEAD
-    constexpr bool NEXT = decltype(next_c)::value;    // a full step st + 1 follows (its stage is ready)
+  constexpr int kWrites = (A_KMAJOR ? 0 : NV) + (B_KMAJOR ? 0 : NV);
+  auto step = [&](auto next_c, auto ahead2_c, int st) {
+    constexpr bool NEXT = decltype(next_c)::value;      // a step st + 1 follows: load it
+    constexpr bool AHEAD2 = decltype(ahead2_c)::value;  // a step st + 2 follows: issue its LDS-DMA A tile
     const uint8_t* cur = stage_ptr(st);
     uint8_t* nxt = stage_ptr(st + 1);
-    constexpr int kLoads = 2 * NV;
-    constexpr int kWrites = (A_KMAJOR ? 0 : NV) + (B_KMAJOR ? 0 : NV);
     // fc: this slice's fragments; fn: the next slice's (or the next step's first)
     auto slice = [&](auto qc, Frags& fc, Frags& fn) {
       constexpr int q = decltype(qc)::value;
       constexpr bool LAST = q == C::kSlices - 1;
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (!LAST) {
+        constexpr bool LOAD = q == 0 && NEXT;
+        constexpr int kLoadsHere = LOAD ? (A_KMAJOR ? 0 : NV) + NV : 0;
         constexpr bool WRITE = q == C::kSlices - 2 && NEXT && kWrites > 0;  // register-held tiles out
         read_frags<C>(cur, arow, brow, fs[q + 1], fn);
-        if constexpr (q == 0 && ISSUE) issue(st + AHEAD);
+        if constexpr (LOAD) {
+          if constexpr (!A_KMAJOR) issue_a(st + 1);
+          issue_b(st + 1);
+        }
         if constexpr (WRITE) {
           if constexpr (!A_KMAJOR) store_tile<C, false>(nxt, t, ra);
           if constexpr (!B_KMAJOR) store_tile<C, false>(nxt + C::kTileBytes, t, rb);
         }
         mfma_16(fc, acc);
-        if constexpr (q == 0 && ISSUE) {
+        if constexpr (kLoadsHere > 0) {
           __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 fragment reads
 #pragma unroll
-          for (int u = 0; u < kLoads; ++u) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one load
+          for (int u = 0; u < kLoadsHere; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 16 / kLoadsHere, 0);  // products
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                // one load
           }
         }
         if constexpr (WRITE) {
@@ -358,30 +359,30 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
         mfma_8(fc, acc, 0);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (NEXT) {
-          // The next step's loads have landed once at most those issued after them (steps st + 2 ..
-          // st + AHEAD, when this step issued) are still in flight.
-          if constexpr (ISSUE) __builtin_amdgcn_s_waitcnt(waitcnt_vm((AHEAD - 1) * (A_KMAJOR + B_KMAJOR) * NV));
-          else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // every load of nxt has landed
           __syncthreads();
           read_frags<C>(nxt, arow, brow, fs[0], fn);
+          if constexpr (A_KMAJOR && AHEAD2) issue_a(st + 2);  // into cur, which the barrier freed
         }
-        __builtin_amdgcn_sched_barrier(0);
         mfma_8(fc, acc, 1);
+        constexpr int kDma = NEXT && AHEAD2 && A_KMAJOR ? NV : 0;
+        if constexpr (kDma > 0) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the next step's first fragment reads
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one product
+            __builtin_amdgcn_sched_group_barrier(0x010, kDma / 8, 0);  // one or two loads
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     };
     slice(std::integral_constant<int, 0>{}, f0, f1);
     slice(std::integral_constant<int, 1>{}, f1, f0);
-    if constexpr (C::kSlices == 4) {
-      slice(std::integral_constant<int, 2>{}, f0, f1);
-      slice(std::integral_constant<int, 3>{}, f1, f0);
-    }
-    // The next step's first fragments (in f0: the slice count is even) have landed while these
-    // products were issued; waiting here keeps the next step's first products from waiting for reads
-    // issued ahead of them.
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    slice(std::integral_constant<int, 2>{}, f0, f1);
+    slice(std::integral_constant<int, 3>{}, f1, f0);
   };
-  static_assert(C::kSlices % 2 == 0, "slices alternate between two fragment sets");
+  static_assert(C::kSlices == 4, "four 16-wide slices per step");
 
   // Steps: a partial one (K not a multiple of BK: the last k range, loaded through registers with
   // masking) goes first, as step 0, so that every step runs through the same pipeline; the full steps
@@ -400,20 +401,20 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
       store_tile<C, A_KMAJOR>(stage_ptr(0), t, ra);
       store_tile<C, B_KMAJOR>(stage_ptr(0) + C::kTileBytes, t, rb);
     } else {
-      issue(0);
+      issue_a(0);
+      issue_b(0);
       if constexpr (!A_KMAJOR) store_tile<C, false>(stage_ptr(0), t, ra);
       if constexpr (!B_KMAJOR) store_tile<C, false>(stage_ptr(0) + C::kTileBytes, t, rb);
     }
-#pragma unroll
-    for (int a = 1; a < AHEAD; ++a)  // (DMA configurations only)
-      if (a < nsteps) issue(a);
+    if constexpr (A_KMAJOR)
+      if (nsteps > 1) issue_a(1);  // the A tile of step 1, two steps ahead of its use like the rest
     first_fragments(stage_ptr(0));
     int st = 0;
 #pragma nounroll
-    for (; st + AHEAD < nsteps; ++st) step(std::true_type{}, std::true_type{}, st);
-    if constexpr (AHEAD > 1) {
-#pragma nounroll
-      for (; st + 1 < nsteps; ++st) step(std::false_type{}, std::true_type{}, st);
+    for (; st + 2 < nsteps; ++st) step(std::true_type{}, std::true_type{}, st);
+    if (st + 1 < nsteps) {
+      step(std::true_type{}, std::false_type{}, st);
+      ++st;
     }
     step(std::false_type{}, std::false_type{}, st);
   }
