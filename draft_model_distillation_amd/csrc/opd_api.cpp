@@ -16,6 +16,7 @@
 #include <string>
 #include <unordered_map>
 
+#include "opd_gemm.h"
 #include "opd_internal.h"
 
 static_assert(OPD_FLAG_NEG_L == opd::kFlagNegL, "flag mismatch");

@@ -30,6 +30,7 @@
 
 #include <type_traits>
 
+#include "opd_gemm.h"
 #include "opd_internal.h"
 
 namespace opd {

@@ -9,6 +9,7 @@
 
 #include <string>
 
+#include "opd_gemm.h"
 #include "opd_internal.h"
 
 namespace opd {
