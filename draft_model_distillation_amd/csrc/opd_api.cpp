@@ -512,9 +512,9 @@ size_t opd_lmhead_scratch_size(int64_t chunk_rows, int64_t vocab, int64_t ld_y) 
   if (chunk_rows <= 0 || vocab <= 0 || ld_y < vocab) return 0;
   // logits chunk: fp32 with the pitch of y (the row kernel reads both with one pitch); dz chunk: bf16,
   // a region that first holds the logits product's row-statistics partials (3 floats per row and
-  // 128-column half tile)
+  // wave column of a 256-column tile)
   const int64_t zb = round_up(chunk_rows * ld_y * 4, 256);
-  const int64_t parts = 2 * ((vocab + opd::kGemmTile - 1) / opd::kGemmTile);
+  const int64_t parts = opd::kGemmStatParts * ((vocab + opd::kGemmTile - 1) / opd::kGemmTile);
   const int64_t db = round_up(std::max(chunk_rows * round_up(vocab, 8) * 2, chunk_rows * parts * 12), 256);
   return (size_t)(zb + db);
 }
@@ -559,11 +559,11 @@ static opd_status_t opd_lmhead_fused_fwd_bwd_verify_impl(const void* h, const vo
   float* zc = static_cast<float*>(scratch);
   uint16_t* dzc = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(scratch) + round_up(rc_max * ld_y * 4, 256));
   // The dz region holds the logits product's row-statistics partials until the row kernel writes dz
-  // (rc x 2 ceil(V / 256) x 3 floats, well under rc x ld_dz bf16), and the logits region holds the
+  // (rc x kGemmStatParts ceil(V / 256) x 3 floats, well under rc x ld_dz bf16), and the logits region holds the
   // split dh product's partials once the row kernel has read the logits (k_split x rc x hidden floats).
   float* zstats = reinterpret_cast<float*>(dzc);
   const bool want_stats = logit_max_lse || logit_argmax;
-  const int n_parts = 2 * (int)((vocab + opd::kGemmTile - 1) / opd::kGemmTile);
+  const int n_parts = opd::kGemmStatParts * (int)((vocab + opd::kGemmTile - 1) / opd::kGemmTile);
   const uint16_t* Wb = static_cast<const uint16_t*>(W);
   const uint8_t* hb = static_cast<const uint8_t*>(h);
   const uint8_t* yb = static_cast<const uint8_t*>(y);

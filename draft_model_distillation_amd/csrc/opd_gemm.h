@@ -15,8 +15,10 @@ namespace opd {
 // bases 16-byte aligned and each operand smaller than 4 GiB (K-major rows may hold anything past K:
 // those values are masked). k_split > 1 splits K over that many workgroup slices whose partial
 // products go to `partial` ([k_split][M][ldc] fp32) and are summed in slice order. `stats` (K-major
-// operands only) receives per row and per 128-column half tile (max, lowest index of it as int bits,
-// sum of exp(c - max)): [M][2 * ceil(N / 256)][3].
+// operands only) receives per row and per wave column of a tile (kGemmStatParts per 256 columns: max,
+// lowest index of it as int bits, sum of exp(c - max)): [M][kGemmStatParts * ceil(N / 256)][3].
+constexpr int kGemmWaves = 4;                      // waves per workgroup of the product kernel (8 also built: no faster)
+constexpr int kGemmStatParts = kGemmWaves / 2;     // statistics partials per 256-column tile
 struct GemmParams {
   const uint16_t* A;
   int64_t lda;
@@ -44,8 +46,8 @@ hipError_t launch_zstats_reduce(const float* part, int n_parts, int M, float* ma
 // C[M, N] (pitch ldc) = sum_k A(m, k) B(k, n) (+ beta C) on the MFMA kernels, layouts as GemmParams
 // (opd_lmhead.cpp): checks sizes, pitches and the 32-bit offset limits, then launches. k_split > 1
 // needs `partial` (k_split x M x ldc floats; beta is applied in the reduction); `stats` (nullable,
-// unsplit both-K-major products only) receives the row-statistics partials, M x 2 ceil(N / 256) x 3
-// floats, for launch_zstats_reduce.
+// unsplit both-K-major products only) receives the row-statistics partials, M x kGemmStatParts
+// ceil(N / 256) x 3 floats, for launch_zstats_reduce.
 opd_status_t gemm_bf16_f32(const uint16_t* A, int64_t lda, bool a_kmajor, const uint16_t* B, int64_t ldb,
                            bool b_kmajor, int64_t M, int64_t N, int64_t K, float beta, float* C, int64_t ldc,
                            int k_split, float* partial, float* stats, hipStream_t stream);

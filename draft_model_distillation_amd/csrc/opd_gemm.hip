@@ -41,7 +41,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256;
-constexpr int kGemmThreads = 256;
+// Waves of a workgroup: kGemmWaves / 2 along N, 2 along M. Each wave computes 128 rows x kWaveCols
+// columns of the tile: 4 x FJ blocks of 32 x 32 accumulators.
+constexpr int kWaves = kGemmWaves;
+constexpr int kGemmThreads = 64 * kWaves;
+constexpr int kWavesN = kWaves / 2;
+constexpr int FI = 4;                    // 32-row A fragments per wave
+constexpr int FJ = 8 / kWavesN;          // 32-column B fragments per wave
+constexpr int kWaveCols = 32 * FJ;
+constexpr int kSliceMfma = FI * FJ;      // products per wave per 16-wide k slice
+static_assert(kWaves == 4 || kWaves == 8, "four or eight waves");
+static_assert(kGemmStatParts == kWavesN, "one statistics partial per wave column");
 constexpr int kLdsBytes = 128 * 1024;  // two stages of 64 KiB
 
 // Pipeline shape of a product and the derived sizes (one shape for all products: K step 64, two LDS
@@ -54,7 +64,7 @@ struct Cfg {
   static constexpr int kRowBytes = 2 * BK;               // one LDS tile row
   static constexpr int kTileBytes = 256 * kRowBytes;     // one operand tile
   static constexpr int kStageBytes = 2 * kTileBytes;     // A and B
-  static constexpr int kVecs = BK / 8;                   // 16-byte vectors per thread per operand tile
+  static constexpr int kVecs = 256 * BK / 8 / kGemmThreads;  // 16-byte vectors per thread per operand tile
   static constexpr int kSlices = BK / 16;                // 16-wide k slices per step
   static constexpr int kRowVecs = BK / 8;                // 16-byte vectors per tile row
   static constexpr int kInstrRows = 1024 / kRowBytes;    // tile rows one LDS-DMA instruction fills
@@ -103,6 +113,18 @@ template <class C, bool KMAJOR>
 __device__ __forceinline__ int kmajor_kvec(int t, int i) {
   return ((t & 63) % C::kRowVecs) ^ swz<C::BK>(kmajor_row<C, KMAJOR>(t, i));
 }
+// M/N-major: the k (within the step) of vector i and the first of the thread's 8 tile rows. Four
+// waves: k = 8 (t / 32) + i (8 k values: a whole k vector per row), rows 8 (t % 32). Eight waves:
+// lane l of wave w covers k vector w, half l & 1 (k = 8 w + 4 (l & 1) + i, 4 k values per row),
+// rows 8 (l >> 1).
+__device__ __forceinline__ int mn_k(int t, int i) {
+  if constexpr (kWaves == 4) return 8 * (t / 32) + i;
+  else return 8 * (t >> 6) + 4 * (t & 1) + i;
+}
+__device__ __forceinline__ int mn_row(int t) {
+  if constexpr (kWaves == 4) return 8 * (t % 32);
+  else return 8 * ((t & 63) >> 1);
+}
 template <class C, bool KMAJOR>
 __device__ __forceinline__ void tile_offsets(uint32_t ld_bytes, int row0, int k0, int t, uint32_t (&off)[C::kVecs]) {
 #pragma unroll
@@ -111,7 +133,7 @@ __device__ __forceinline__ void tile_offsets(uint32_t ld_bytes, int row0, int k0
       off[i] = (uint32_t)(row0 + kmajor_row<C, KMAJOR>(t, i)) * ld_bytes + 2u * (uint32_t)k0 +
                16u * (uint32_t)kmajor_kvec<C, KMAJOR>(t, i);
     } else {
-      off[i] = (uint32_t)(k0 + 8 * (t / 32) + i) * ld_bytes + 2u * (uint32_t)(row0 + 8 * (t % 32));
+      off[i] = (uint32_t)(k0 + mn_k(t, i)) * ld_bytes + 2u * (uint32_t)(row0 + mn_row(t));
     }
   }
 }
@@ -144,7 +166,7 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t r, const uint32
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = 2 * e + 1 < n ? x[e] : 2 * e < n ? (x[e] & 0xffffu) : 0u;
       } else {
-        if (k0 + 8 * (t / 32) + i >= kend) x = u32x4{0, 0, 0, 0};
+        if (k0 + mn_k(t, i) >= kend) x = u32x4{0, 0, 0, 0};
       }
     }
     v[i] = x;
@@ -158,7 +180,7 @@ __device__ __forceinline__ void store_tile(uint8_t* tile, int t, const u32x4 (&v
 #pragma unroll
     for (int i = 0; i < C::kVecs; ++i)
       *reinterpret_cast<u32x4*>(tile + 1024 * ((t >> 6) * C::kVecs + i) + 16 * (t & 63)) = v[i];
-  } else {
+  } else if constexpr (kWaves == 4) {
     // v[i] holds rows 8 g .. 8 g + 7 at k = 8 q + i (g = t % 32, q = t / 32); each of the 8 rows gets
     // its 8 k values (k vector q) as one 16-byte write (byte permutes pick the rows' halves)
     const int g = t % 32, q = t / 32;
@@ -174,6 +196,21 @@ __device__ __forceinline__ void store_tile(uint8_t* tile, int t, const u32x4 (&v
       *reinterpret_cast<u32x4*>(tile + r0 * C::kRowBytes + 16 * (q ^ swz<C::BK>(r0))) = lo;
       *reinterpret_cast<u32x4*>(tile + r1 * C::kRowBytes + 16 * (q ^ swz<C::BK>(r1))) = hi;
     }
+  } else {
+    // v[i] holds rows 8 g .. 8 g + 7 at k = 8 q + 4 h + i (g = l >> 1, h = l & 1, q = the wave); each
+    // of the 8 rows gets its 4 k values as one 8-byte write into half h of its k vector q
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const int g = (t & 63) >> 1, h = t & 1, q = t >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x2 lo = {__builtin_amdgcn_perm(v[1][j], v[0][j], 0x05040100u),
+                        __builtin_amdgcn_perm(v[3][j], v[2][j], 0x05040100u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(v[1][j], v[0][j], 0x07060302u),
+                        __builtin_amdgcn_perm(v[3][j], v[2][j], 0x07060302u)};
+      const int r0 = 8 * g + 2 * j, r1 = r0 + 1;
+      *reinterpret_cast<u32x2*>(tile + r0 * C::kRowBytes + 16 * (q ^ swz<C::BK>(r0)) + 8 * h) = lo;
+      *reinterpret_cast<u32x2*>(tile + r1 * C::kRowBytes + 16 * (q ^ swz<C::BK>(r1)) + 8 * h) = hi;
+    }
   }
 }
 
@@ -183,30 +220,31 @@ __device__ __forceinline__ void store_tile(uint8_t* tile, int t, const u32x4 (&v
 // slice's k vector in that row. Rows 32 i further on (the halves start at multiples of 128 rows, where
 // the swizzles vanish) are swizzled alike for 64-byte rows and by an extra 2 i for 128-byte rows.
 struct Frags {
-  bf16x8 a[4], b[4];
+  bf16x8 a[FI], b[FJ];
 };
 template <class C>
-__device__ __forceinline__ void read_frags(const uint8_t* stage, uint32_t arow, uint32_t brow, uint32_t slot, Frags& f) {
-  constexpr uint32_t kX = C::BK == 64 ? 2 : 0;
+__device__ __forceinline__ void read_frags(const uint8_t* stage, uint32_t arow, uint32_t brow, uint32_t slot,
+                                           uint32_t bx, Frags& f) {
+  static_assert(C::BK == 64, "128-byte rows");
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
     f.a[i] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u32x4*>(stage + arow + 32 * i * C::kRowBytes + 16 * (slot ^ (kX * i))));
+        bf16x8, *reinterpret_cast<const u32x4*>(stage + arow + 32 * i * C::kRowBytes + 16 * (slot ^ (2 * i))));
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < FJ; ++j)
     f.b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + C::kTileBytes + brow + 32 * j * C::kRowBytes +
-                                                                           16 * (slot ^ (kX * j))));
+                                                                           16 * (slot ^ bx ^ (2 * j))));
 }
-// Half of the 16 products of one slice: A fragments 2 h and 2 h + 1.
-__device__ __forceinline__ void mfma_8(const Frags& f, f32x16 (&acc)[4][4], int h) {
+// Half of one slice's products: A fragments 2 h and 2 h + 1.
+__device__ __forceinline__ void mfma_half(const Frags& f, f32x16 (&acc)[FI][FJ], int h) {
 #pragma unroll
   for (int i = 2 * h; i < 2 * h + 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < FJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
-__device__ __forceinline__ void mfma_16(const Frags& f, f32x16 (&acc)[4][4]) {
-  mfma_8(f, acc, 0);
-  mfma_8(f, acc, 1);
+__device__ __forceinline__ void mfma_slice(const Frags& f, f32x16 (&acc)[FI][FJ]) {
+  mfma_half(f, acc, 0);
+  mfma_half(f, acc, 1);
 }
 
 // Row statistics of one 32 x 32 output block row-group over a lane's columns: see the epilogue.
@@ -235,6 +273,25 @@ __device__ __forceinline__ int half_min(int v) {
   return min((int)p[0], (int)p[1]);
 }
 
+// Scheduling-group order for one slice's products interleaved with NOTHER other instructions of the
+// class MASK (0x010 vector-memory loads, 0x200 LDS writes), spread evenly.
+template <int NPROD, int NOTHER, int MASK>
+__device__ __forceinline__ void interleave() {
+  if constexpr (NOTHER > 0 && NOTHER <= NPROD) {
+#pragma unroll
+    for (int u = 0; u < NOTHER; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NPROD / NOTHER, 0);
+      __builtin_amdgcn_sched_group_barrier(MASK, 1, 0);
+    }
+  } else if constexpr (NOTHER > NPROD) {
+#pragma unroll
+    for (int u = 0; u < NPROD; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(MASK, NOTHER / NPROD, 0);
+    }
+  }
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitLgkm0 = 0xC07F;
@@ -246,7 +303,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int t = (int)__builtin_amdgcn_workitem_id_x();
   const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 1, wn = wave & 1;  // this wave's 128 x 128 quarter of the tile
+  const int wm = wave / kWavesN, wn = wave % kWavesN;  // this wave's 128 x kWaveCols part of the tile
 
   // Tile order: the M tiles of one N tile run on the same XCD (workgroups are dispatched to the XCDs
   // round-robin), so that they share the N tile's operand block in that XCD's L2.
@@ -261,11 +318,11 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
   const int nsteps = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
   const int nfull = (kend - kbeg) / BK;  // steps that need no masking
 
-  f32x16 acc[4][4];
+  f32x16 acc[FI][FJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < FJ; ++j) acc[i][j] = f32x16{};
 
   const __amdgpu_buffer_rsrc_t rA = operand_rsrc(P.A, P.a_bytes);
   const __amdgpu_buffer_rsrc_t rB = operand_rsrc(P.B, P.b_bytes);
@@ -293,10 +350,13 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
 
   // Fragment rows: row l % 32 of the wave's halves; slice q reads k vector 2 q + l / 32.
   const int fr = lane & 31, fh = lane >> 5;
-  const uint32_t arow = (uint32_t)(wm * 128 + fr) * C::kRowBytes, brow = (uint32_t)(wn * 128 + fr) * C::kRowBytes;
+  const uint32_t arow = (uint32_t)(wm * 128 + fr) * C::kRowBytes,
+                 brow = (uint32_t)(wn * kWaveCols + fr) * C::kRowBytes;
   uint32_t fs[C::kSlices];
 #pragma unroll
   for (int q = 0; q < C::kSlices; ++q) fs[q] = (uint32_t)((2 * q + fh) ^ swz<BK>(fr));
+  // the swizzle's higher term at the wave's first B row (A halves start at multiples of 128 rows)
+  const uint32_t bx = (uint32_t)(((wn * kWaveCols) >> 4) & 7);
 
   // Step st computes from stage st % 2 (cur) while the next step's tiles arrive in the other (nxt):
   //   - an LDS-DMA A tile (K-major A) is issued two steps ahead, right after the barrier of the step
@@ -312,10 +372,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
   auto first_fragments = [&](const uint8_t* stage) {
     __builtin_amdgcn_s_waitcnt(0);  // every load so far (LDS-DMA included) has landed
     __syncthreads();
-    read_frags<C>(stage, arow, brow, fs[0], f0);
+    read_frags<C>(stage, arow, brow, fs[0], bx, f0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   };
-  constexpr int kWrites = (A_KMAJOR ? 0 : NV) + (B_KMAJOR ? 0 : NV);
+  constexpr int kWrites = (A_KMAJOR ? 0 : 8) + (B_KMAJOR ? 0 : 8);  // one per tile row a thread holds
   auto step = [&](auto next_c, auto ahead2_c, int st) {
     constexpr bool NEXT = decltype(next_c)::value;      // a step st + 1 follows: load it
     constexpr bool AHEAD2 = decltype(ahead2_c)::value;  // a step st + 2 follows: issue its LDS-DMA A tile
@@ -330,7 +390,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
         constexpr bool LOAD = q == 0 && NEXT;
         constexpr int kLoadsHere = LOAD ? (A_KMAJOR ? 0 : NV) + NV : 0;
         constexpr bool WRITE = q == C::kSlices - 2 && NEXT && kWrites > 0;  // register-held tiles out
-        read_frags<C>(cur, arow, brow, fs[q + 1], fn);
+        read_frags<C>(cur, arow, brow, fs[q + 1], bx, fn);
         if constexpr (LOAD) {
           if constexpr (!A_KMAJOR) issue_a(st + 1);
           issue_b(st + 1);
@@ -339,41 +399,29 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
           if constexpr (!A_KMAJOR) store_tile<C, false>(nxt, t, ra);
           if constexpr (!B_KMAJOR) store_tile<C, false>(nxt + C::kTileBytes, t, rb);
         }
-        mfma_16(fc, acc);
+        mfma_slice(fc, acc);
         if constexpr (kLoadsHere > 0) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 fragment reads
-#pragma unroll
-          for (int u = 0; u < kLoadsHere; ++u) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 16 / kLoadsHere, 0);  // products
-            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                // one load
-          }
+          __builtin_amdgcn_sched_group_barrier(0x100, FI + FJ, 0);  // the fragment reads
+          interleave<kSliceMfma, kLoadsHere, 0x010>();
         }
         if constexpr (WRITE) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 fragment reads
-#pragma unroll
-          for (int u = 0; u < kWrites; ++u) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one 16-byte LDS write
-          }
+          __builtin_amdgcn_sched_group_barrier(0x100, FI + FJ, 0);  // the fragment reads
+          interleave<kSliceMfma, kWrites, 0x200>();
         }
       } else {
-        mfma_8(fc, acc, 0);
+        mfma_half(fc, acc, 0);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (NEXT) {
           __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // every load of nxt has landed
           __syncthreads();
-          read_frags<C>(nxt, arow, brow, fs[0], fn);
+          read_frags<C>(nxt, arow, brow, fs[0], bx, fn);
           if constexpr (A_KMAJOR && AHEAD2) issue_a(st + 2);  // into cur, which the barrier freed
         }
-        mfma_8(fc, acc, 1);
+        mfma_half(fc, acc, 1);
         constexpr int kDma = NEXT && AHEAD2 && A_KMAJOR ? NV : 0;
         if constexpr (kDma > 0) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the next step's first fragment reads
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one product
-            __builtin_amdgcn_sched_group_barrier(0x010, kDma / 8, 0);  // one or two loads
-          }
+          __builtin_amdgcn_sched_group_barrier(0x100, FI + FJ, 0);  // the next step's first fragment reads
+          interleave<kSliceMfma / 2, kDma, 0x010>();
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -432,15 +480,15 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
       uniform_ptr(out + corner), 0, __builtin_amdgcn_readfirstlane((int)(remain < 0xFFFFFFFFll ? remain : 0xFFFFFFFFll)),
       0x00020000);
   const uint32_t ldc4 = 4u * (uint32_t)P.ldc;
-  const uint32_t lane_off = (uint32_t)(wm * 128 + rq) * ldc4 + 4u * (uint32_t)(wn * 128 + col);
-  bool nok[4];
+  const uint32_t lane_off = (uint32_t)(wm * 128 + rq) * ldc4 + 4u * (uint32_t)(wn * kWaveCols + col);
+  bool nok[FJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) nok[j] = n0 + wn * 128 + 32 * j + col < P.N;
+  for (int j = 0; j < FJ; ++j) nok[j] = n0 + wn * kWaveCols + 32 * j + col < P.N;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < FJ; ++j) {
     if (nok[j]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t off = lane_off + (uint32_t)(32 * i + 8 * (r / 4) + (r % 4)) * ldc4 + 128u * j;
@@ -451,23 +499,27 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
     }
   }
   if constexpr (STATS) {
-    // Per row of this wave's quarter: max over its (valid) 128 columns, the lowest column holding it,
-    // and the sum of exp(c - max). Lanes l and l + 32 hold different rows; the 32 lanes of a half hold
-    // the 32 columns of a block, four blocks per lane.
-    float* st_base = P.stats + (2 * n_tile + wn) * 3;
-    const int64_t st_ld = 2 * P.n_tiles * 3;
+    // Per row of this wave's part: max over its (valid) kWaveCols columns, the lowest column holding
+    // it, and the sum of exp(c - max). Lanes l and l + 32 hold different rows; the 32 lanes of a half
+    // hold the 32 columns of a block, FJ blocks per lane.
+    float* st_base = P.stats + (kGemmStatParts * n_tile + wn) * 3;
+    const int64_t st_ld = kGemmStatParts * P.n_tiles * 3;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FI; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float v[4];
+        float v[FJ];
+        float lm = -__builtin_inff();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = nok[j] ? acc[i][j][r] : -__builtin_inff();
-        const float mx = half_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-        int li = 0x7fffffff;  // lowest column (relative to the wave's half tile) holding the max
+        for (int j = 0; j < FJ; ++j) {
+          v[j] = nok[j] ? acc[i][j][r] : -__builtin_inff();
+          lm = fmaxf(lm, v[j]);
+        }
+        const float mx = half_max(lm);
+        int li = 0x7fffffff;  // lowest column (relative to the wave's part) holding the max
         float ls = 0.f;
 #pragma unroll
-        for (int j = 3; j >= 0; --j) {
+        for (int j = FJ - 1; j >= 0; --j) {
           if (v[j] == mx) li = 32 * j + col;
           ls += nok[j] ? __expf(v[j] - mx) : 0.f;
         }
@@ -477,7 +529,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
         if (col == 0 && m < P.M) {
           float* stp = st_base + (int64_t)m * st_ld;
           stp[0] = mx;
-          stp[1] = __int_as_float(ix + n0 + wn * 128);
+          stp[1] = __int_as_float(ix + n0 + wn * kWaveCols);
           stp[2] = sm;
         }
       }
