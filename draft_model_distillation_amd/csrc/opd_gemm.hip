@@ -7,24 +7,24 @@
 // needs when the drafter's vocabulary projection is trained with it.
 //
 // One kernel template: C[m, n] = sum_k A(m, k) B(k, n) (+ beta C), bf16 operands, fp32 accumulation
-// with v_mfma_f32_32x32x16_bf16. Workgroup tile 256 x 256, four waves of 128 x 128 (4 x 4 blocks of
-// 32 x 32: 256 accumulators per lane, all in the accumulation registers), one workgroup per CU. Each
-// operand tile is staged in LDS as [m or n][k] with rows of BK bf16 whose 16-byte k vectors are
+// with v_mfma_f32_32x32x16_bf16. Workgroup tile 256 x 256, one workgroup per CU, kGemmWaves waves
+// (four: 128 x 128 each, 4 x 4 blocks of 32 x 32 = 256 accumulators per lane, all in the accumulation
+// registers; eight, two per SIMD, 128 x 64 each, is also written and measured no faster). Each
+// operand tile is staged in LDS as [m or n][k] with rows of 64 bf16 whose 16-byte k vectors are
 // XOR-swizzled by the row, so that fragment reads and tile writes spread over the LDS banks.
 //   K-major operand (global [m][K]): loaded straight into LDS (buffer loads with the LDS-DMA bit:
 //   lane l of an instruction fills 16 bytes at l * 16), the lanes choosing their global vector so that
 //   the linear LDS image is the swizzled tile. No registers, no LDS write instructions.
-//   M/N-major operand (global [K][m]): 16-byte loads along m into registers; each thread holds 8 k x
-//   8 m values and writes them transposed (byte permutes, 16-byte LDS writes) between the products.
-// K step 64 and two LDS stages: the loads of step s + 1 are issued during step s (one per product of
-// its first k slice). A ring of four 32-wide stages (loads three steps ahead) is also implemented for
-// the both-K-major product, but measured slower. A partial K step (K not a multiple of the step) is
-// loaded through registers with the values past K zeroed and runs first, so that every step goes
-// through the same pipeline.
+//   M/N-major operand (global [K][m]): 16-byte loads along m into registers, written transposed
+//   (byte permutes) between the products.
+// K step 64 and two LDS stages with one barrier per step: an LDS-DMA A tile is issued two steps
+// ahead (right after the barrier that frees its stage), the B tile and register-held tiles one step
+// ahead. A partial K step (K not a multiple of 64) is loaded through registers with the values past
+// K zeroed and runs first, so that every step goes through the same pipeline.
 // MFMA operand fragments (lane l: row l % 32, k = 8 (l / 32) + 0..7) are single 16-byte LDS reads.
-// Optional epilogue (the logits product): per row and per 128-column half tile, the maximum, the lowest
-// column index holding it and the sum of exp(c - max), written as partials that k_zstats_reduce
-// combines in a fixed order into per-row max, argmax and log-sum-exp.
+// Optional epilogue (the logits product): per row and per wave column of the tile, the maximum, the
+// lowest column index holding it and the sum of exp(c - max), written as partials that
+// k_zstats_reduce combines in a fixed order into per-row max, argmax and log-sum-exp.
 
 #include <stdint.h>
 
@@ -55,8 +55,8 @@ static_assert(kGemmStatParts == kWavesN, "one statistics partial per wave column
 constexpr int kLdsBytes = 128 * 1024;  // two stages of 64 KiB
 
 // Pipeline shape of a product and the derived sizes (one shape for all products: K step 64, two LDS
-// stages; a ring of four 32-wide stages for the both-K-major product measured slower, 3.1 against
-// 2.6 ms on the 2048 x 151936 x 4096 logits product).
+// stages; a ring of four 32-wide stages with loads three steps ahead was measured slower on the
+// 2048 x 151936 x 4096 logits product, 3.1 against 2.6 ms, and removed).
 template <bool A_KMAJOR, bool B_KMAJOR>
 struct Cfg {
   static constexpr int BK = 64;
@@ -73,14 +73,13 @@ struct Cfg {
 
 // LDS position of k vector kv of tile row `row`: 16-byte slot kv ^ swz(row). The LDS serves 16 lanes'
 // 16-byte accesses per cycle from 64 four-byte banks: 16 bank groups of 16 bytes, group
-// (row * kRowVecs + slot) % 16. 64-byte rows (BK 32): (row >> 2) & 3 makes the fragment reads
-// (16 consecutive rows, one k vector) conflict-free. 128-byte rows (BK 64): ((row >> 1) ^ (row >> 4))
-// & 7 makes them conflict-free and keeps the transposed writes of an M/N-major operand (rows 8 g + o
-// for 16 consecutive g) at most 2-way.
+// (8 row + slot) % 16 for 128-byte rows. ((row >> 1) ^ (row >> 4)) & 7 makes the fragment reads
+// (16 consecutive rows, one k vector) conflict-free and keeps the transposed writes of an M/N-major
+// operand (rows 8 g + o for 16 consecutive g) at most 2-way.
 template <int BK>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (BK == 32) return (row >> 2) & 3;
-  else return ((row >> 1) ^ (row >> 4)) & 7;
+  static_assert(BK == 64, "128-byte rows");
+  return ((row >> 1) ^ (row >> 4)) & 7;
 }
 
 // A wave-uniform pointer held in scalar registers (buffer resources must be).
@@ -103,8 +102,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const uint16_t* b
 //   K-major ([row][K], ld bytes per row): vector i is tile row kInstrRows (w kVecs + i) + l / kRowVecs,
 //   LDS slot l % kRowVecs, i.e. global k vector (l % kRowVecs) ^ swz(row); the 64 lanes of vector i
 //   fill 1 KiB of LDS in lane order. A step moves 2 BK bytes along k.
-//   M/N-major ([K][row], BK 64): vector i is k = 8 (t / 32) + i, rows 8 (t % 32) .. + 7; a step moves
-//   BK k-rows.
+//   M/N-major ([K][row]): vector i is k-row mn_k(t, i) of the step, rows mn_row(t) .. + 7; a step
+//   moves BK k-rows.
 template <class C, bool KMAJOR>
 __device__ __forceinline__ int kmajor_row(int t, int i) {
   return C::kInstrRows * ((t >> 6) * C::kVecs + i) + (t & 63) / C::kRowVecs;
