@@ -14,18 +14,21 @@
 // is 297 KiB per tensor, more than one CU can hold, so a row is split over a *team* of G workgroups;
 // each keeps its chunk resident for the whole row (z packed in VGPRs, y in LDS through direct
 // buffer-to-LDS loads), so z and y are read from HBM once and dz written once:
-//   phase A  per 16-byte vector: max z, max y, max(z - y), and sums of 2^(z log2e - c) and of the
-//            same terms times (z - y) relative to the vector's own c = fl(max z log2e); one running
-//            sum of 2^(y log2e - r) per lane
+//   phase A  per 16-byte vector: max z, max y, max(z - y), and sums of 2^(z log2e - r_z) and of
+//            the same terms times (z - y); one running sum of 2^(y log2e - r_y) per lane. r_z, r_y
+//            are the lane's first vector's fl(max log2e) (redone from the lane maxima in the rare lane
+//            whose values climb more than 96 octaves above them)
 //   chunk    maxima, sums rescaled to the chunk maxima
 //   -- exchange 1 --  wave 0 publishes 4 values, gathers all members' and combines them in a fixed
 //                     order: every member derives identical row constants
 //   phase B  S and the clipped reverse KL: vectors whose bound is <= tau provably hold no clipped
-//            term and use their phase-A sums; the rest (near the peak) are visited element by element;
-//            then the chunk's lowest indices of the row maxima (decoded only where a lane holds one)
+//            term and use their phase-A sums; the rest (near the peak) are visited element by element.
+//            A per-lane threshold on max z screens the vectors first, so that the bound and its exp2
+//            are evaluated only near the peak. Then the chunk's lowest indices of the row maxima
+//            (decoded only where a lane holds one)
 //   -- exchange 2 --  the two sums, the two indices and z at the target top-1
 //   phase C  dz written once (bf16 rounded to nearest even, or fp32)
-// The kernel is VALU-heavy for an HBM stream (about 33 VALU instructions per element, 3.5 of them
+// The kernel is VALU-heavy for an HBM stream (about 31 VALU instructions per element, 3.4 of them
 // exponentials), so the per-element work is kept minimal and the per-row work (reductions,
 // exchanges, row constants) runs once per workgroup in wave 0 while the other waves wait at
 // barriers and the SIMDs serve the other resident workgroups. The waves of a CU's workgroups are in
@@ -47,7 +50,8 @@
 // p_v is evaluated from M and log S_z held apart (RowConst), so that large logits keep full fp32
 // relative accuracy. Vectors proven free of clipped terms contribute to S and the reverse KL
 // through their per-vector sums from phase A; vectors near the peak are summed element by element
-// (no cancellation between the clipped terms and the rest). The clip decision is the same fp32
+// and left out of those sums (never subtracted from a total that held them, so there is no
+// cancellation between the clipped terms and the rest). The clip decision is the same fp32
 // test, from the same per-row floats, in the fused and the separate kernels, so fused and
 // forward+backward results are bit-identical.
 
@@ -508,6 +512,32 @@ __device__ __forceinline__ int first_eq(const float (&v)[EPV], float m) {
   return e0;
 }
 
+// Sums of one vector's terms relative to a lane reference: se = sum 2^(x log2e - ref), sb = sum of
+// the same terms times d. Phase A and the element-by-element path of phase B call it with the same
+// operands and get the same floats.
+template <int EPV>
+__device__ __forceinline__ void vec_sums(const float (&x)[EPV], const float (&d)[EPV], float ref, float& se,
+                                         float& sb) {
+  float ez = exp2_fast(__builtin_fmaf(x[0], kLog2e, -ref));
+  se = ez;
+  sb = ez * d[0];
+#pragma unroll
+  for (int e = 1; e < EPV; ++e) {
+    ez = exp2_fast(__builtin_fmaf(x[e], kLog2e, -ref));
+    se += ez;
+    sb = __builtin_fmaf(ez, d[e], sb);
+  }
+}
+
+// Sum of the per-vector values v[k] of a lane in slot order, leaving out the slots set in `skip`.
+template <int K>
+__device__ __forceinline__ float lane_sum(const float (&v)[K], uint32_t skip) {
+  float a = (skip & 1u) ? 0.f : v[0];
+#pragma unroll
+  for (int k = 1; k < K; ++k) a += ((skip >> k) & 1u) ? 0.f : v[k];
+  return a;
+}
+
 // ---------------------------------------------------------------- the row-team kernel
 //
 // A team of G workgroups owns a row; workgroup `chunk` owns vectors [cv0, cv0 + clen) of it, each
@@ -665,7 +695,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     // The ln index is made opaque once per row: otherwise the compiler hoists every per-slot and
     // per-element ln test (sentinels, validity, offsets) out of the row loop and keeps them all
     // live in registers.
-    int lt = (wave << 6) + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    // (mbcnt counts from the opaque zero, so that the lane number is not hoisted out of the loop
+    // and held across it either)
+    int lt = (wave << 6) + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, (uint32_t)z0));
     __asm__ volatile("" : "+v"(lt));
     const int voff = lt * 16;
     const int ln = lt & 63, wv = lt >> 6;
@@ -701,8 +733,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     }
 
     // ---- phase A
-    float lzmax = kNegInf;
-    float ek[K], bk[K];
+    // Per lane: the maxima of z, y and z - y over its vectors, and three sums relative to the lane's
+    // own references (2^fl(max log2 e) of its first vector's z and y): of 2^(z log2e - ref_z), of
+    // the same terms times (z - y), and of 2^(y log2e - ref_y). A lane whose maximum climbs more than
+    // 96 octaves above its first vector's redoes its sums from its maximum (rare: the terms could
+    // otherwise approach the end of the fp32 range).
+    float lzmax = kNegInf, ldmax = kNegInf;
+    float ek[K], bk[K];  // per-vector sums relative to ref_z
+    float ref_z = 0.f;
     float lymax = kNegInf, sy = 0.f, ref_y = 0.f;
     int kym = 0;
 #pragma unroll
@@ -723,36 +761,41 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       }
 #pragma unroll
       for (int e = 0; e < EPV; ++e) d[e] = x[e] - w[e];
-      const float zmax = vmax<EPV>(x);
+      const float zmax = vmax<EPV>(x), dmax = vmax<EPV>(d);
       {
         VecMax<EPV> vk;
-        vk.set(zmax, vmax<EPV>(d));
+        vk.set(zmax, dmax);
         vmlds[k * kThreads + lt] = vk;  // kept in LDS until phase B (registers are the scarce resource)
       }
       lzmax = fmaxf(lzmax, zmax);
       if constexpr (kSums) {
-        const float cz = zmax * kLog2e;
-        float ez = exp2_fast(__builtin_fmaf(x[0], kLog2e, -cz));
-        float se = ez, sb = ez * d[0];
-#pragma unroll
-        for (int e = 1; e < EPV; ++e) {
-          ez = exp2_fast(__builtin_fmaf(x[e], kLog2e, -cz));
-          se += ez;
-          sb = __builtin_fmaf(ez, d[e], sb);
-        }
-        ek[k] = se;
-        bk[k] = sb;
+        ldmax = fmaxf(ldmax, dmax);
+        if (k == 0) ref_z = zmax * kLog2e;
+        vec_sums<EPV>(x, d, ref_z, ek[k], bk[k]);
         fence_vals(ek[k], bk[k], sy);
       }
       fence_vals(lzmax);
       fence_vals(lymax);
     }
     if constexpr (kSums) {
-      // the y sum is relative to the first vector's maximum: redo it from the ln maximum where y
-      // rose so far above it that the terms could approach the fp32 range (rare)
-      const bool redo = lymax * kLog2e - ref_y > 96.f;
-      if (__builtin_amdgcn_ballot_w64(redo)) {
-        if (redo) {
+      const bool redo_z = lzmax * kLog2e - ref_z > 96.f;
+      const bool redo_y = lymax * kLog2e - ref_y > 96.f;
+      if (__builtin_amdgcn_ballot_w64(redo_z || redo_y)) {
+        if (redo_z) {
+          ref_z = lzmax * kLog2e;
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            opaque(zr[k]);
+            float x[EPV], w[EPV], d[EPV];
+            In::decode(zr[k], x);
+            In::decode(ylds[k * kThreads + lt], w);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) d[e] = x[e] - w[e];
+            vec_sums<EPV>(x, d, ref_z, ek[k], bk[k]);
+            fence_vals(ek[k], bk[k]);
+          }
+        }
+        if (redo_y) {
           ref_y = lymax * kLog2e;
           sy = 0.f;
 #pragma unroll
@@ -787,11 +830,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     float wsz = 0.f, wsy = 0.f;
     if constexpr (kSums) {
       const float cMz = Mzc * kLog2e, cMy = Myc * kLog2e;
-      float lsz = ek[0] * exp2_fast(vmlds[lt].z() * kLog2e - cMz);
-#pragma unroll
-      for (int k = 1; k < K; ++k)
-        lsz = __builtin_fmaf(ek[k], exp2_fast(vmlds[k * kThreads + lt].z() * kLog2e - cMz), lsz);
-      wsz = wsum(lsz);
+      wsz = wsum(lane_sum<K>(ek, 0u) * exp2_fast(ref_z - cMz));
       wsy = wsum(sy * exp2_fast(ref_y - cMy));
     }
     int wiz = kBig, wiy = kBig;
@@ -986,37 +1025,53 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       // are summed element by element. Phase B feeds the second exchange: it runs above phases A
       // and C, and the reduction and exchange above that.
       __builtin_amdgcn_s_setprio(2);
-      float pe = 0.f, pb = 0.f, s_slow = 0.f, r_slow = 0.f;
+      // Screening: a vector whose max z is at most zt passes the exact bound test below (the
+      // vector_may_clip test, shared with k_bwd) with room to spare, since its bound
+      // sc max(dmax - delta, 0) is at most 2^-1.49 tau_b when every dmax of the lane is counted at
+      // the lane's largest; only vectors above zt evaluate the exact test and its exp2, so the set
+      // of vectors summed element by element is exactly that of the exact test. tau_b below
+      // 2^-100 (including tau <= 0) sends every vector to the exact test.
+      const float m_l = fmaxf(kept_dmax<EPV>(ldmax) - delta, 0.f);
+      float zt = kNegInf;
+      if (tau_b >= 0x1p-100f)
+        zt = m_l == 0.f ? -kNegInf
+                        : ((rc.c_hi + rc.c_lo) + ((log2_fast(tau_b) - log2_fast(fmaxf(m_l, 0x1p-100f))) - 1.5f)) * kLn2;
+      float s_slow = 0.f, r_slow = 0.f;
       uint32_t slowbits = 0;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const VecMax<EPV> vk = vmlds[k * kThreads + lt];
-        const float sc = vector_scale(rc, vk.z());
-        const bool slow = vector_may_clip(rc, sc, vk.d(), tau_b);
-        slowbits |= (uint32_t)slow << k;
-        const float u = slow ? 0.f : sc;
-        pe = __builtin_fmaf(u, ek[k], pe);
-        pb = __builtin_fmaf(u, bk[k], pb);
-        fence_vals(pe, pb);  // the vector's scale is dead before the element-by-element path
-        if (__builtin_amdgcn_ballot_w64(slow)) {
-          opaque(zr[k]);
-          float x[EPV], w[EPV];
-          In::decode(zr[k], x);
-          In::decode(ylds[k * kThreads + lt], w);
-          const int vi = cv0 + lt + k * kThreads;
-          const int nvalid = (lt + k * kThreads < clen) ? min(EPV, pp->vocab - vi * EPV) : 0;
+        const bool near = vk.z() > zt;
+        if (__builtin_amdgcn_ballot_w64(near)) {
+          const bool slow = near && vector_may_clip(rc, vector_scale(rc, vk.z()), vk.d(), tau_b);
+          if (__builtin_amdgcn_ballot_w64(slow)) {
+            slowbits |= (uint32_t)slow << k;
+            opaque(zr[k]);
+            float x[EPV], w[EPV], d[EPV];
+            In::decode(zr[k], x);
+            In::decode(ylds[k * kThreads + lt], w);
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) {
-            const bool valid = slow && e < nvalid;
-            const float p = rc.p(x[e]);
-            const float t = p * ((x[e] - w[e]) - delta);
-            const bool clipped = t > tau;
-            r_slow += valid ? (clipped ? tau : t) : 0.f;
-            s_slow += (valid && !clipped) ? (t + p) : 0.f;
+            for (int e = 0; e < EPV; ++e) d[e] = x[e] - w[e];
+            const int vi = cv0 + lt + k * kThreads;
+            const int nvalid = (lt + k * kThreads < clen) ? min(EPV, pp->vocab - vi * EPV) : 0;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+              const bool valid = slow && e < nvalid;
+              const float p = rc.p(x[e]);
+              const float t = p * (d[e] - delta);
+              const bool clipped = t > tau;
+              r_slow += valid ? (clipped ? tau : t) : 0.f;
+              s_slow += (valid && !clipped) ? (t + p) : 0.f;
+            }
+            fence_vals(r_slow, s_slow);
           }
-          fence_vals(r_slow, s_slow);
         }
       }
+      // Sums of the vectors that pass, scaled from the lane reference to p. The vectors summed
+      // element by element are left out rather than subtracted from a total: a subtraction would
+      // cancel when such a vector dominates its lane.
+      const float scl = exp2_fast((ref_z - rc.c_hi) - rc.c_lo);
+      const float pe = lane_sum<K>(ek, slowbits) * scl, pb = lane_sum<K>(bk, slowbits) * scl;
       __builtin_amdgcn_s_setprio(3);
       // lowest indices of the row maxima within this chunk (kBig where the chunk does not reach
       // them), and z at the one of y: only waves holding a row maximum decode, which is usually one
@@ -1025,7 +1080,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       float wza = 0.f;
       {
         const float Myr = sh.row[z0 + kRowMy];
-        int kk = K;
+        int kk = K;  // the lane's first slot holding the row maximum of z
 #pragma unroll
         for (int k = K - 1; k >= 0; --k) kk = (vmlds[k * kThreads + lt].z() == Mz) ? k : kk;
         const bool hz = kk < K;
@@ -1125,8 +1180,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         dc.init(rc, sh.row[z0 + kRowS], alpha, pp->grad_loss ? pp->grad_loss[row] : 1.f);
         const __amdgpu_buffer_rsrc_t rd = rsrc(pp->dz + (int64_t)row * pp->ld_dz_bytes + (int64_t)cv0 * VB, clen * VB);
         __asm__ volatile("" : "+v"(lt));  // fresh offsets: not kept live from the loads
-        // the one vector holding the target top-1 (if it lies in this chunk), from exchange 2
-        const int atop = __float_as_int(sh.row[z0 + kRowAtop]);
+        // the one vector holding the target top-1 (if it lies in this chunk), from exchange 2; the
+        // index is the same in every lane, so it is moved to a scalar register and the slot test
+        // below is scalar code
+        const int atop = __builtin_amdgcn_readfirstlane(__float_as_int(sh.row[z0 + kRowAtop]));
         const int va = atop / EPV - cv0;
         const int ka = (va >= 0 && va < clen) ? va / kThreads : -1;
 #pragma unroll

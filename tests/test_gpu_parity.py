@@ -422,6 +422,38 @@ def test_identical_rows_and_large_logits(lib):
         assert ok, f"row {r}: {msg}"
 
 
+@pytest.mark.parametrize("dtype_name", ["bf16", "f32"])
+def test_clipped_peak_beside_large_passing_terms(lib, dtype_name):
+    """A clipped term with a huge z - y (p ~ 0.9, z - y ~ 9000) near many unclipped terms whose
+    p (z - y) is far from negligible. S has to leave the clipped term out exactly: taking it out of a
+    sum that held it would cancel to about an ulp of 9000, well past the dz tolerance."""
+    import torch
+
+    rng = np.random.default_rng(33)
+    v = 151936
+    z = rng.normal(0, 1, size=(2, v)).astype(np.float32)
+    y = z.copy()
+    peak = 30611
+    z[0, peak], y[0, peak] = 20.0, -9000.0
+    for j in range(1, 9):  # neighbours at multiples of 1024 logits: the lane stride of the row plans
+        for i in (peak - 1024 * j, peak + 1024 * j):
+            z[0, i], y[0, i] = 15.0, 65.0
+    z[1] = z[0][::-1]
+    y[1] = y[0][::-1]
+    zt, zx = _to_dev_padded(z, v, dtype_name)
+    yt, yx = _to_dev_padded(y, v, dtype_name)
+    _say(f"clipped peak beside large passing terms {dtype_name}")
+    out = lib.opd_fused_fwd_bwd_verify(zt, yt, None, None, 0.5, 0.05, dz_dtype=torch.float32)
+    torch.cuda.synchronize()
+    loss = out["loss"].cpu().numpy()
+    dz = out["dz"].cpu().numpy().astype(np.float64)
+    for r in range(2):
+        dz_ref, info = O.row_grad(zx[r], yx[r], 0.5, 0.05, 1.0)
+        assert info["clipped"][peak if r == 0 else v - 1 - peak]
+        ok, msg = parity.check_row(zx[r], yx[r], 0.5, 0.05, loss[r], dz[r])
+        assert ok, f"row {r}: {msg}"
+
+
 def test_accept_length_edge_cases(lib):
     import torch
 
