@@ -35,6 +35,7 @@ struct GemmParams {
   float* partial;   // k_split > 1
   float* stats;     // nullable
   int m_tiles, n_tiles;  // set by launch_gemm
+  int m_major;            // set by launch_gemm: tile order keeps the N tiles of one M tile on one XCD
 };
 hipError_t launch_gemm(GemmParams p, bool a_kmajor, bool b_kmajor, hipStream_t s);
 size_t gemm_lds_bytes();

@@ -304,13 +304,22 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmParams P) {
   const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave / kWavesN, wn = wave % kWavesN;  // this wave's 128 x kWaveCols part of the tile
 
-  // Tile order: the M tiles of one N tile run on the same XCD (workgroups are dispatched to the XCDs
-  // round-robin), so that they share the N tile's operand block in that XCD's L2.
+  // Tile order: the tiles that share a block of the larger operand run on the same XCD (workgroups
+  // are dispatched to the XCDs round-robin), so that they read it from that XCD's L2: the M tiles of
+  // one N tile when B is the larger operand (more N tiles than M tiles), else the N tiles of one M
+  // tile.
   const int b = (int)__builtin_amdgcn_workgroup_id_x();
-  const int mt = P.m_tiles;
   const int xcd = b % 8, s = b / 8;
-  const int n_tile = 8 * (s / mt) + xcd, m_tile = s % mt;
-  if (n_tile >= P.n_tiles) return;  // padding of the tile order (uniform per workgroup)
+  int m_tile, n_tile;
+  if (P.m_major) {
+    m_tile = 8 * (s / P.n_tiles) + xcd;
+    n_tile = s % P.n_tiles;
+    if (m_tile >= P.m_tiles) return;  // padding of the tile order (uniform per workgroup)
+  } else {
+    n_tile = 8 * (s / P.m_tiles) + xcd;
+    m_tile = s % P.m_tiles;
+    if (n_tile >= P.n_tiles) return;
+  }
   const int m0 = m_tile * BM, n0 = n_tile * BN;
   const int kz = (int)__builtin_amdgcn_workgroup_id_y();
   const int kbeg = kz * P.kslice, kend = min(P.K, kbeg + P.kslice);
@@ -606,7 +615,8 @@ hipError_t launch_gemm(GemmParams p, bool a_kmajor, bool b_kmajor, hipStream_t s
   // more than 64 KiB of dynamic LDS (set on every launch: the setting is per device)
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (e != hipSuccess) return e;
-  const int grid = 8 * p.m_tiles * ((p.n_tiles + 7) / 8);
+  p.m_major = p.m_tiles > p.n_tiles;
+  const int grid = p.m_major ? 8 * p.n_tiles * ((p.m_tiles + 7) / 8) : 8 * p.m_tiles * ((p.n_tiles + 7) / 8);
   void* args[] = {&p};
   e = hipLaunchKernel((const void*)k, dim3(grid, p.k_split), dim3(kGemmThreads), args, kLdsBytes, s);
   if (e != hipSuccess) return e;
