@@ -38,7 +38,6 @@ struct GemmParams {
   int m_major;            // set by launch_gemm: tile order keeps the N tiles of one M tile on one XCD
 };
 hipError_t launch_gemm(GemmParams p, bool a_kmajor, bool b_kmajor, hipStream_t s);
-size_t gemm_lds_bytes();
 constexpr int kGemmTile = 256;
 // Per-row (max, log-sum-exp) pairs and lowest argmax from the product's statistics partials (either
 // output may be NULL).

@@ -599,8 +599,6 @@ GemmKernel kernel_of() {
 
 }  // namespace
 
-size_t gemm_lds_bytes() { return kLdsBytes; }
-
 hipError_t launch_gemm(GemmParams p, bool a_kmajor, bool b_kmajor, hipStream_t s) {
   p.m_tiles = (p.M + BM - 1) / BM;
   p.n_tiles = (p.N + BN - 1) / BN;
