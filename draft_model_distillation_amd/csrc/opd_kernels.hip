@@ -80,7 +80,7 @@ __device__ __forceinline__ int block_id_y() { return (int)__builtin_amdgcn_workg
 
 struct F32In {
   static constexpr int EPV = 4;
-  static constexpr int kWavesPerEU = 4;  // 4 workgroups per CU: LDS (34.5 KB each) allows no more
+  static constexpr int kWavesPerEU = 5;  // 5 workgroups per CU: LDS (27.9 KB each) allows no more
   // -32768 (exact in fp32 and bf16): never a maximum and e^(s - max) underflows to 0, because inputs
   // satisfy |logit| <= 1e4; small enough that s log2(e) keeps a tiny absolute rounding error (a
   // vector made only of sentinels is reduced relative to its own maximum, the sentinel itself).
@@ -407,7 +407,8 @@ struct DzConst {
 // most p(max x) max(max(x - y) - delta, 0). p(max x) is replaced by sc = 2^(fl(max x log2 e) - c_hi -
 // c_lo), the factor that also scales the vector's phase-A sums; the two differ by a factor below
 // 1.003 for |x| <= 1e4, so the test runs against tau / 1.01: a vector that passes holds no term above
-// tau. The same test, from the same floats, runs in the fused and the backward kernels.
+// tau (max x is kept rounded up for fp32 inputs, which only raises sc). The same test, from the same
+// floats, runs in the fused and the backward kernels.
 constexpr float kBoundShrink = 1.f / 1.01f;
 __device__ __forceinline__ float vector_scale(const RowConst& rc, float zmax) {
   return exp2_fast((zmax * kLog2e - rc.c_hi) - rc.c_lo);
@@ -460,21 +461,23 @@ __device__ __forceinline__ void fence_vals(float& a, float& b, float& c, float& 
 }
 
 
-// Per-vector maxima kept from phase A to phase B: max z and max(z - y). For bf16 inputs both fit one
-// register: max z is itself a bf16 value (exact), and max(z - y) is rounded up to bf16, which only
-// loosens the phase-B bound (the backward kernel applies the same rounding, so decisions agree).
-template <int EPV>
-struct VecMax {
-  float zm, dm;
-  __device__ __forceinline__ void set(float z, float d) { zm = z; dm = d; }
-  __device__ __forceinline__ float z() const { return zm; }
-  __device__ __forceinline__ float d() const { return dm; }
-  __device__ __forceinline__ void fence() { __asm__ volatile("" : "+v"(zm), "+v"(dm)); }
-};
+// Per-vector maxima kept from phase A to phase B: max z and max(z - y), both in one 32-bit word as
+// two bf16. max(z - y) is rounded up, which only loosens the phase-B bound; so is max z for fp32
+// inputs (for bf16 inputs it is itself a bf16 value, exact). The backward kernel applies the same
+// roundings, so the two kernels decide alike. Where the exact max z is needed (the top-1 search), it
+// comes from the resident chunk for fp32 inputs (slot_holds_max).
 __device__ __forceinline__ uint32_t bf16_bits_up(float d) {  // bits of the least bf16 >= d (finite d)
   const uint32_t u = __float_as_uint(d);
   return (int32_t)u >= 0 ? (u + 0xffffu) & 0xffff0000u : u & 0xffff0000u;
 }
+template <int EPV>
+struct VecMax {
+  uint32_t pk;  // [max(z - y) rounded up : 16][max z rounded up : 16]
+  __device__ __forceinline__ void set(float z, float d) { pk = (bf16_bits_up(z) >> 16) | bf16_bits_up(d); }
+  __device__ __forceinline__ float z() const { return __uint_as_float(pk << 16); }
+  __device__ __forceinline__ float d() const { return __uint_as_float(pk & 0xffff0000u); }
+  __device__ __forceinline__ void fence() { __asm__ volatile("" : "+v"(pk)); }
+};
 template <>
 struct VecMax<8> {
   uint32_t pk;  // [max(z - y) rounded up : 16][max z : 16]
@@ -483,11 +486,15 @@ struct VecMax<8> {
   __device__ __forceinline__ float d() const { return __uint_as_float(pk & 0xffff0000u); }
   __device__ __forceinline__ void fence() { __asm__ volatile("" : "+v"(pk)); }
 };
-// The bound's max(z - y) as the fused kernel keeps it (see VecMax).
+// The bound's max(z - y) and max z as the fused kernel keeps them (see VecMax).
 template <int EPV>
 __device__ __forceinline__ float kept_dmax(float d) {
-  if constexpr (EPV == 8) return __uint_as_float(bf16_bits_up(d));
-  else return d;
+  return __uint_as_float(bf16_bits_up(d));
+}
+template <int EPV>
+__device__ __forceinline__ float kept_zmax(float z) {
+  if constexpr (EPV == 8) return z;
+  else return __uint_as_float(bf16_bits_up(z));
 }
 
 // Sum of the EPV values of a vector in a fixed pairwise order.
@@ -510,6 +517,19 @@ __device__ __forceinline__ int first_eq(const float (&v)[EPV], float m) {
 #pragma unroll
   for (int e = EPV - 1; e >= 0; --e) e0 = (v[e] == m) ? e : e0;
   return e0;
+}
+
+// Whether a vector holds the value m as its maximum of z: from the kept maximum where that is exact
+// (bf16 inputs), else from the resident vector itself.
+template <class In>
+__device__ __forceinline__ bool holds_zmax(const VecMax<In::EPV>& v, const uint4& raw, float m) {
+  if constexpr (In::EPV == 8) {
+    return v.z() == m;
+  } else {
+    float x[In::EPV];
+    In::decode(raw, x);
+    return vmax<In::EPV>(x) == m;
+  }
 }
 
 // Sums of one vector's terms relative to a lane reference: se = sum 2^(x log2e - ref), sb = sum of
@@ -840,7 +860,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       if (__builtin_amdgcn_ballot_w64(hz)) {  // a wave holding the chunk maximum of z
         int kk = K;
 #pragma unroll
-        for (int k = K - 1; k >= 0; --k) kk = (vmlds[k * kThreads + lt].z() == Mzc) ? k : kk;
+        for (int k = K - 1; k >= 0; --k) kk = holds_zmax<In>(vmlds[k * kThreads + lt], zr[k], Mzc) ? k : kk;
         int iz = kBig;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -1082,7 +1102,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         const float Myr = sh.row[z0 + kRowMy];
         int kk = K;  // the lane's first slot holding the row maximum of z
 #pragma unroll
-        for (int k = K - 1; k >= 0; --k) kk = (vmlds[k * kThreads + lt].z() == Mz) ? k : kk;
+        for (int k = K - 1; k >= 0; --k) kk = holds_zmax<In>(vmlds[k * kThreads + lt], zr[k], Mz) ? k : kk;
         const bool hz = kk < K;
         if (__builtin_amdgcn_ballot_w64(hz)) {
           int iz = kBig;
@@ -1303,7 +1323,7 @@ __global__ void __launch_bounds__(kThreads) k_bwd(BwdParams P) {
     float d[EPV];
 #pragma unroll
     for (int e = 0; e < EPV; ++e) d[e] = x[e] - w[e];
-    const float sc = vector_scale(rc, vmax<EPV>(x));
+    const float sc = vector_scale(rc, kept_zmax<EPV>(vmax<EPV>(x)));
     const bool slow = vector_may_clip(rc, sc, kept_dmax<EPV>(vmax<EPV>(d)), tau * kBoundShrink);
     dz_vector<EPV>(x, w, slow, __builtin_amdgcn_ballot_w64(slow) != 0, rc, dc, tau, o);
     const int g0 = vi * EPV;
