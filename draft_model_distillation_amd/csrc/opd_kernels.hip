@@ -366,6 +366,45 @@ __device__ __forceinline__ int wmin(int v) {
   return __builtin_amdgcn_readfirstlane(min(a, b));
 }
 
+// Two independent full-wave reductions in one register (all 64 lanes active): v_permlane32_swap
+// between the two values leaves a's lanes l and l + 32 in lane l < 32 and b's in lane l + 32, so one
+// combine halves both; v_permlane16_swap then brings the two rows of each half together, and four
+// in-row DPP steps finish: lane 0 holds a's result, lane 32 b's. Half the instructions of two single
+// reductions. Sums in a fixed order: for each lane l of a row, (x_l + x_{l+32}) + (x_{l+16} + x_{l+48}),
+// then the in-row steps.
+template <class F>
+__device__ __forceinline__ int wreduce2(int a, int b, F op, int& rb) {
+  const auto p = __builtin_amdgcn_permlane32_swap(a, b, false, false);  // {[a_lo, b_lo], [a_hi, b_hi]}
+  int v = op((int)p[0], (int)p[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // rows 0|1 and 2|3 of each half
+  v = op((int)q[0], (int)q[1]);
+  v = op(v, dpp_row<0xB1>(v));
+  v = op(v, dpp_row<0x4E>(v));
+  v = op(v, dpp_row<0x141>(v));
+  v = op(v, dpp_row<0x140>(v));
+  rb = __builtin_amdgcn_readlane(v, 32);
+  return __builtin_amdgcn_readlane(v, 0);
+}
+__device__ __forceinline__ void wsum2(float& a, float& b) {
+  int rb;
+  const int ra = wreduce2(__float_as_int(a), __float_as_int(b),
+                          [](int x, int y) { return __float_as_int(__int_as_float(x) + __int_as_float(y)); }, rb);
+  a = __int_as_float(ra);
+  b = __int_as_float(rb);
+}
+__device__ __forceinline__ void wmax2(float& a, float& b) {
+  int rb;
+  const int ra = wreduce2(__float_as_int(a), __float_as_int(b),
+                          [](int x, int y) { return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y))); }, rb);
+  a = __int_as_float(ra);
+  b = __int_as_float(rb);
+}
+__device__ __forceinline__ void wmin2(int& a, int& b) {
+  int rb;
+  a = wreduce2(a, b, [](int x, int y) { return min(x, y); }, rb);
+  b = rb;
+}
+
 // ---------------------------------------------------------------- per-row constants
 
 // Probability of a logit x under the row's softmax, p(x) = exp(x - LSE(z)), evaluated as
@@ -549,12 +588,20 @@ __device__ __forceinline__ void vec_sums(const float (&x)[EPV], const float (&d)
   }
 }
 
-// Sum of the per-vector values v[k] of a lane in slot order, leaving out the slots set in `skip`.
+// Sum of the per-vector values v[k] of a lane in slot order; the second form leaves out the slots
+// whose `skip` is set (each a lane mask, so a slot costs one select).
 template <int K>
-__device__ __forceinline__ float lane_sum(const float (&v)[K], uint32_t skip) {
-  float a = (skip & 1u) ? 0.f : v[0];
+__device__ __forceinline__ float lane_sum(const float (&v)[K]) {
+  float a = v[0];
 #pragma unroll
-  for (int k = 1; k < K; ++k) a += ((skip >> k) & 1u) ? 0.f : v[k];
+  for (int k = 1; k < K; ++k) a += v[k];
+  return a;
+}
+template <int K>
+__device__ __forceinline__ float lane_sum(const float (&v)[K], const bool (&skip)[K]) {
+  float a = skip[0] ? 0.f : v[0];
+#pragma unroll
+  for (int k = 1; k < K; ++k) a += skip[k] ? 0.f : v[k];
   return a;
 }
 
@@ -653,10 +700,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
           lza = __uint_as_float(u[4]);
         }
       }
-      S = wsum(ls);
-      rkl = wsum(lr);
-      dtop = wmin(liz);
-      atop = wmin(liy);
+      wsum2(ls, lr);
+      S = ls;
+      rkl = lr;
+      dtop = liz;
+      atop = liy;
+      wmin2(dtop, atop);
       za = wsum(liy == atop ? lza : 0.f);
     }
     if (ln_ == 0) {
@@ -836,7 +885,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     // the other workgroups sharing the CU, and drop it once the row constants arrive.
     __builtin_amdgcn_s_setprio(3);
     {
-      const float a = wmax(lzmax), c = wmax(lymax);
+      float a = lzmax, c = lymax;
+      wmax2(a, c);
       if (ln == 0) {
         sh.wred[wv][z0 + 0] = a;
         sh.wred[wv][z0 + 1] = c;
@@ -850,8 +900,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     float wsz = 0.f, wsy = 0.f;
     if constexpr (kSums) {
       const float cMz = Mzc * kLog2e, cMy = Myc * kLog2e;
-      wsz = wsum(lane_sum<K>(ek, 0u) * exp2_fast(ref_z - cMz));
-      wsy = wsum(sy * exp2_fast(ref_y - cMy));
+      wsz = lane_sum<K>(ek) * exp2_fast(ref_z - cMz);
+      wsy = sy * exp2_fast(ref_y - cMy);
+      wsum2(wsz, wsy);
     }
     int wiz = kBig, wiy = kBig;
     float wza = 0.f;
@@ -967,8 +1018,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
           mz = fmaxf(mz, __uint_as_float(sh.rx[z0 + c * NU1 + 0]));
           my = fmaxf(my, __uint_as_float(sh.rx[z0 + c * NU1 + kMy]));
         }
-        Mz = wmax(mz);
-        My = wmax(my);
+        wmax2(mz, my);
+        Mz = mz;
+        My = my;
         const float cHz = Mz * kLog2e, cHy = My * kLog2e;
         for (int c = ln; c < G; c += 64) {
           const uint32_t* u = sh.rx + z0 + c * NU1;
@@ -985,13 +1037,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
           }
         }
         if constexpr (kSums) {
-          Sz = wsum(lsz);
-          Sy = wsum(lsy);
+          wsum2(lsz, lsy);
+          Sz = lsz;
+          Sy = lsy;
           dtop = atop = kBig;  // from exchange 2
           za = 0.f;
         } else {
-          dtop = wmin(liz);
-          atop = wmin(liy);
+          dtop = liz;
+          atop = liy;
+          wmin2(dtop, atop);
           za = wsum(liy == atop ? lza : 0.f);
         }
       } else {
@@ -1057,15 +1111,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         zt = m_l == 0.f ? -kNegInf
                         : ((rc.c_hi + rc.c_lo) + ((log2_fast(tau_b) - log2_fast(fmaxf(m_l, 0x1p-100f))) - 1.5f)) * kLn2;
       float s_slow = 0.f, r_slow = 0.f;
-      uint32_t slowbits = 0;
+      bool slow_k[K];  // per slot: the lane's vector is summed element by element (a lane mask each)
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const VecMax<EPV> vk = vmlds[k * kThreads + lt];
         const bool near = vk.z() > zt;
+        slow_k[k] = false;
         if (__builtin_amdgcn_ballot_w64(near)) {
           const bool slow = near && vector_may_clip(rc, vector_scale(rc, vk.z()), vk.d(), tau_b);
           if (__builtin_amdgcn_ballot_w64(slow)) {
-            slowbits |= (uint32_t)slow << k;
+            slow_k[k] = slow;
             opaque(zr[k]);
             float x[EPV], w[EPV], d[EPV];
             In::decode(zr[k], x);
@@ -1091,7 +1146,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       // element by element are left out rather than subtracted from a total: a subtraction would
       // cancel when such a vector dominates its lane.
       const float scl = exp2_fast((ref_z - rc.c_hi) - rc.c_lo);
-      const float pe = lane_sum<K>(ek, slowbits) * scl, pb = lane_sum<K>(bk, slowbits) * scl;
+      const float pe = lane_sum<K>(ek, slow_k) * scl, pb = lane_sum<K>(bk, slow_k) * scl;
       __builtin_amdgcn_s_setprio(3);
       // lowest indices of the row maxima within this chunk (kBig where the chunk does not reach
       // them), and z at the one of y: only waves holding a row maximum decode, which is usually one
@@ -1143,8 +1198,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         }
       }
       {
-        const float a = wsum(__builtin_fmaf(1.f - delta, pe, pb) + s_slow);
-        const float c = wsum(__builtin_fmaf(-delta, pe, pb) + r_slow);
+        float a = __builtin_fmaf(1.f - delta, pe, pb) + s_slow;
+        float c = __builtin_fmaf(-delta, pe, pb) + r_slow;
+        wsum2(a, c);
         if (ln == 0) {
           sh.wred[wv][z0 + 0] = a;
           sh.wred[wv][z0 + 1] = c;
@@ -1212,7 +1268,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
           float x[EPV], w[EPV], o[EPV];
           In::decode(zr[k], x);
           In::decode(ylds[k * kThreads + lt], w);
-          const bool slow = (slowbits >> k) & 1u;
+          const bool slow = slow_k[k];
           dz_vector<EPV>(x, w, slow, __builtin_amdgcn_ballot_w64(slow) != 0, rc, dc, tau, o);
           const int vi = cv0 + lt + k * kThreads;
           if (k == ka) fix_target<EPV>(o, vi * EPV, atop, dc.wce);
