@@ -35,7 +35,8 @@
 // different phases of different rows, and the issue priority of each phase (s_setprio) orders them
 // by how much of the team they hold up: the chunk reductions and both exchanges 3 (all G members
 // of the team wait on them), phase B 2 (it feeds the second exchange), phase C 1 (it ends the row
-// and frees the workgroup for its next loads), the loads and phase A 0. Exchanges use 8-byte
+// and frees the workgroup for its next loads), the issue of the next row's loads 2 (a short burst
+// that must not wait behind the other workgroups), phase A 0. Exchanges use 8-byte
 // [value | flag] units written and polled with agent-scope relaxed atomics (sc1: coherent across
 // XCDs without L2 writeback / invalidate); the flag is unique per launch, row iteration and stage,
 // so nothing has to be reset between launches and a stale unit can never be taken for a fresh one.
@@ -744,7 +745,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
   int iter = 0;
   for (int row = team; row < P.n_rows; row += P.n_teams, ++iter) {
     __syncthreads();  // the previous row is done with ylds and sh
-    __builtin_amdgcn_s_setprio(0);  // loads and phase A: the lowest issue priority
+    // The row's loads go out at a raised issue priority (their address arithmetic must not wait
+    // behind the other workgroups' phases); phase A then runs at the lowest.
+    __builtin_amdgcn_s_setprio(2);
     // Kernel arguments are re-read (scalar loads) in every row instead of occupying scalar registers
     // for the whole loop.
     KParams* pp = (KParams*)__builtin_amdgcn_kernarg_segment_ptr();
@@ -775,8 +778,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
 #pragma unroll
     for (int k = 0; k < K; ++k) {  // every load of the chunk in flight at once
       zr[k] = buf_load16(rz, voff + k * (16 * kThreads));
-      buf_load16_lds(ry, voff + k * (16 * kThreads), ylds + k * kThreads + wv * 64);
+      buf_load16_lds(ry, voff + k * (16 * kThreads), ylds + k * kThreads + wave * 64);
     }
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
