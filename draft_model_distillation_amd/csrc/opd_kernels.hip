@@ -1517,6 +1517,8 @@ hipError_t launch_team(const TeamParams& p, int mode, int in_bf16, int out_bf16,
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
+constexpr int kTeamMaxPerCu = 6;
+
 hipError_t team_occupancy(int mode, int in_bf16, int out_bf16, int K, bool dev_flags, int* blocks_per_cu) {
   const void* fn = team_kernel_any(mode, in_bf16, out_bf16, K, dev_flags);
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kThreads, 0);
@@ -1537,6 +1539,12 @@ hipError_t team_occupancy(int mode, int in_bf16, int out_bf16, int K, bool dev_f
     const int by_lds = (int)((size_t)lds_cu / lds);
     if (by_lds < *blocks_per_cu) *blocks_per_cu = by_lds;
   }
+  // Nor does the count include the trap handler's 16 scalar registers that every wave holds on this
+  // part beside its own (allocated in granules of 16, at most 112): with 800 per SIMD, a wave using
+  // 97-112 leaves room for 6 per SIMD, not the 7 the runtime reports (a team kernel with 104
+  // measured one workgroup per CU short: its teams waited for members that were not resident).
+  // One wave per SIMD per workgroup, so 6 workgroups per CU hold for any scalar register use.
+  if (*blocks_per_cu > kTeamMaxPerCu) *blocks_per_cu = kTeamMaxPerCu;
   return hipSuccess;
 }
 
