@@ -502,35 +502,26 @@ __device__ __forceinline__ void fence_vals(float& a, float& b, float& c, float& 
 
 
 // Per-vector maxima kept from phase A to phase B: max z and max(z - y), both in one 32-bit word as
-// two bf16. max(z - y) is kept as max(max(z - y), 0) rounded up, which only loosens the phase-B
-// bound (it needs max(z - y) - delta from above); with the clamp the rounding is one add, and
-// v_perm_b32 joins the two high halves. max z is rounded up too for fp32 inputs (for bf16 inputs it
-// is itself a bf16 value, exact). The backward kernel applies the same roundings, so the two kernels
-// decide alike. Where the exact max z is needed (the top-1 search), it comes from the resident
-// chunk for fp32 inputs (holds_zmax).
+// two bf16. max(z - y) is rounded up, which only loosens the phase-B bound; so is max z for fp32
+// inputs (for bf16 inputs it is itself a bf16 value, exact). The backward kernel applies the same
+// roundings, so the two kernels decide alike. Where the exact max z is needed (the top-1 search), it
+// comes from the resident chunk for fp32 inputs (slot_holds_max).
 __device__ __forceinline__ uint32_t bf16_bits_up(float d) {  // bits of the least bf16 >= d (finite d)
   const uint32_t u = __float_as_uint(d);
   return (int32_t)u >= 0 ? (u + 0xffffu) & 0xffff0000u : u & 0xffff0000u;
 }
-// The high half of the result is the least bf16 >= d, for d >= 0 (or -0).
-__device__ __forceinline__ uint32_t bf16_up_pos(float d) { return __float_as_uint(d) + 0xffffu; }
-// [high half of hi : 16][high half of lo : 16]
-__device__ __forceinline__ uint32_t join_high_halves(uint32_t hi, uint32_t lo) {
-  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
-}
 template <int EPV>
 struct VecMax {
-  uint32_t pk;  // [max(max(z - y), 0) rounded up : 16][max z rounded up : 16]
-  // d >= 0: the vector's max(z - y) clamped at 0
-  __device__ __forceinline__ void set(float z, float d) { pk = join_high_halves(bf16_up_pos(d), bf16_bits_up(z)); }
+  uint32_t pk;  // [max(z - y) rounded up : 16][max z rounded up : 16]
+  __device__ __forceinline__ void set(float z, float d) { pk = (bf16_bits_up(z) >> 16) | bf16_bits_up(d); }
   __device__ __forceinline__ float z() const { return __uint_as_float(pk << 16); }
   __device__ __forceinline__ float d() const { return __uint_as_float(pk & 0xffff0000u); }
   __device__ __forceinline__ void fence() { __asm__ volatile("" : "+v"(pk)); }
 };
 template <>
 struct VecMax<8> {
-  uint32_t pk;  // [max(max(z - y), 0) rounded up : 16][max z : 16]
-  __device__ __forceinline__ void set(float z, float d) { pk = join_high_halves(bf16_up_pos(d), __float_as_uint(z)); }
+  uint32_t pk;  // [max(z - y) rounded up : 16][max z : 16]
+  __device__ __forceinline__ void set(float z, float d) { pk = (__float_as_uint(z) >> 16) | bf16_bits_up(d); }
   __device__ __forceinline__ float z() const { return __uint_as_float(pk << 16); }
   __device__ __forceinline__ float d() const { return __uint_as_float(pk & 0xffff0000u); }
   __device__ __forceinline__ void fence() { __asm__ volatile("" : "+v"(pk)); }
@@ -538,7 +529,7 @@ struct VecMax<8> {
 // The bound's max(z - y) and max z as the fused kernel keeps them (see VecMax).
 template <int EPV>
 __device__ __forceinline__ float kept_dmax(float d) {
-  return __uint_as_float(bf16_up_pos(fmaxf(d, 0.f)) & 0xffff0000u);
+  return __uint_as_float(bf16_bits_up(d));
 }
 template <int EPV>
 __device__ __forceinline__ float kept_zmax(float z) {
@@ -555,14 +546,6 @@ __device__ __forceinline__ float vsum(const float (&v)[EPV]) {
 template <int EPV>
 __device__ __forceinline__ float vmax(const float (&v)[EPV]) {
   float m = fmaxf(v[0], v[1]);
-#pragma unroll
-  for (int e = 2; e < EPV; ++e) m = fmaxf(m, v[e]);
-  return m;
-}
-// max(0, v[0], ..., v[EPV-1]) (the clamp folds into the first three-input max)
-template <int EPV>
-__device__ __forceinline__ float vmax_pos(const float (&v)[EPV]) {
-  float m = fmaxf(fmaxf(v[0], v[1]), 0.f);
 #pragma unroll
   for (int e = 2; e < EPV; ++e) m = fmaxf(m, v[e]);
   return m;
@@ -587,20 +570,6 @@ __device__ __forceinline__ bool holds_zmax(const VecMax<In::EPV>& v, const uint4
     In::decode(raw, x);
     return vmax<In::EPV>(x) == m;
   }
-}
-
-// The lane's first slot whose vector of y (resident in LDS) has the maximum m (K if none); only the
-// waves holding a row or chunk maximum of y call it.
-template <class In, int K>
-__device__ __forceinline__ int first_slot_holding(const uint4* ylds, int lt, float m) {
-  int kk = K;
-#pragma unroll 1
-  for (int k = K - 1; k >= 0; --k) {  // one vector live at a time
-    float w[In::EPV];
-    In::decode(ylds[k * kThreads + lt], w);
-    kk = vmax<In::EPV>(w) == m ? k : kk;
-  }
-  return kk;
 }
 
 // Sums of one vector's terms relative to a lane reference: se = sum 2^(x log2e - ref), sb = sum of
@@ -846,6 +815,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
     float ek[K], bk[K];  // per-vector sums relative to ref_z
     float ref_z = 0.f;
     float lymax = kNegInf, sy = 0.f, ref_y = 0.f;
+    int kym = 0;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       opaque(zr[k]);
@@ -853,6 +823,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       In::decode(zr[k], x);
       In::decode(ylds[k * kThreads + lt], w);
       const float ym = vmax<EPV>(w);
+      kym = (k == 0 || ym > lymax) ? k : kym;  // first slot holding the lane's maximum of y
       lymax = fmaxf(lymax, ym);
       if constexpr (kSums) {
         if (k == 0) ref_y = ym * kLog2e;
@@ -863,7 +834,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       }
 #pragma unroll
       for (int e = 0; e < EPV; ++e) d[e] = x[e] - w[e];
-      const float zmax = vmax<EPV>(x), dmax = vmax_pos<EPV>(d);
+      const float zmax = vmax<EPV>(x), dmax = vmax<EPV>(d);
       {
         VecMax<EPV> vk;
         vk.set(zmax, dmax);
@@ -960,7 +931,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
       }
       const bool hy = lymax == Myc;
       if (__builtin_amdgcn_ballot_w64(hy)) {
-        const int kk = first_slot_holding<In, K>(ylds, lt, Myc);
+        const int kk = kym;
         int iy = kBig;
         float za = 0.f;
 #pragma unroll
@@ -1208,7 +1179,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(I
         }
         const bool hy = lymax == Myr;
         if (__builtin_amdgcn_ballot_w64(hy)) {
-          const int kym = first_slot_holding<In, K>(ylds, lt, Myr);
           int iy = kBig;
           float za = 0.f;
 #pragma unroll
