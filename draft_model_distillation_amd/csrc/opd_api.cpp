@@ -138,16 +138,23 @@ struct Geometry {
   int K, G, chunk_vec, nvec, n_teams, grid;
 };
 
-// Split a row of nvec 16-byte vectors over G workgroups of 256 threads x K slots each, and choose
-// how many rows (teams) are in flight so that the whole grid is co-resident.
-opd_status_t plan_k(int mode, int in_bf16, int out_bf16, int dev_flags, int K, int nvec, int64_t n_rows, Geometry* g) {
-  const int kidx = K == 1 ? 0 : K == 3 ? 1 : 2;
+// Workgroups per row (team size) and vectors per chunk for K slots per thread.
+int team_geometry(int K, int nvec, int* chunk_vec) {
   const int slots = opd::kThreads * K;
   int G = (nvec + slots - 1) / slots;
   int chunk = (nvec + G - 1) / G;
   chunk = ((chunk + 7) / 8) * 8;  // chunk boundaries on 128-byte lines
   if (chunk > slots) chunk = slots;
-  G = (nvec + chunk - 1) / chunk;
+  if (chunk_vec) *chunk_vec = chunk;
+  return (nvec + chunk - 1) / chunk;
+}
+
+// Split a row of nvec 16-byte vectors over G workgroups of 256 threads x K slots each, and choose
+// how many rows (teams) are in flight so that the whole grid is co-resident.
+opd_status_t plan_k(int mode, int in_bf16, int out_bf16, int dev_flags, int K, int nvec, int64_t n_rows, Geometry* g) {
+  const int kidx = K == 1 ? 0 : K == 3 ? 1 : 2;
+  int chunk = 0;
+  const int G = team_geometry(K, nvec, &chunk);
   if (G > opd::kMaxTeamSize) return fail(OPD_ERR_SHAPE, "vocab too large for one team");
   int cus = 0, occ = 0;
   opd_status_t s = device_info(mode, in_bf16, out_bf16, kidx, K, dev_flags, &cus, &occ);
@@ -174,9 +181,12 @@ opd_status_t plan(int mode, int in_bf16, int out_bf16, int dev_flags, int64_t n_
   const int epv = in_bf16 ? 8 : 4;
   const int nvec = (int)((vocab + epv - 1) / epv);
   if (nvec <= opd::kThreads) return plan_k(mode, in_bf16, out_bf16, dev_flags, 1, nvec, n_rows, g);
-  opd_status_t s = plan_k(mode, in_bf16, out_bf16, dev_flags, 3, nvec, n_rows, g);
-  if (s != OPD_OK) return s;
-  if (g->n_teams >= n_rows) return OPD_OK;
+  // (the three-slot plan only where its team fits: fp32 rows past 393,216 logits need five slots)
+  if (team_geometry(3, nvec, nullptr) <= opd::kMaxTeamSize) {
+    opd_status_t s = plan_k(mode, in_bf16, out_bf16, dev_flags, 3, nvec, n_rows, g);
+    if (s != OPD_OK) return s;
+    if (g->n_teams >= n_rows) return OPD_OK;
+  }
   return plan_k(mode, in_bf16, out_bf16, dev_flags, 5, nvec, n_rows, g);
 }
 

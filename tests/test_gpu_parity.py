@@ -236,8 +236,11 @@ def _to_dev_padded(x, ld, dtype_name):
 
 
 @pytest.mark.parametrize("dtype_name", ["f32", "bf16"])
-@pytest.mark.parametrize("v", [1, 7, 8, 9, 63, 64, 65, 1000, 2049, 10241, 151937])
+@pytest.mark.parametrize("v", [1, 7, 8, 9, 63, 64, 65, 1000, 2049, 10241, 151937, 393220, 524288])
 def test_vocab_sizes_and_padding(lib, dtype_name, v):
+    """Rows of every width class up to the 2^19 limit, in padded rows: one slot per thread, three
+    slots, and rows too wide for a three-slot team (fp32 past 393,216 logits: five slots, 103
+    workgroups at the limit, so the exchange combines take two members per lane)."""
     import torch
 
     rng = np.random.default_rng(v)
