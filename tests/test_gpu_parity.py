@@ -269,6 +269,42 @@ def test_vocab_sizes_and_padding(lib, dtype_name, v):
         assert ok, f"row {r}: {msg}"
 
 
+@pytest.mark.parametrize("dtype_name", ["f32", "bf16"])
+def test_widest_rows_separate_calls_match_fused(lib, dtype_name):
+    """Rows at the 2^19-logit limit through the separate entry points: forward (deferred exchange 2),
+    backward and the top-1 mode (five values per member, several gather passes at 103 members for
+    fp32) give bitwise the fused call's results, which match the oracle."""
+    import torch
+
+    v, n = 1 << 19, 4
+    rng = np.random.default_rng(19)
+    z, y = _random_rows(rng, n, v)
+    zt, zx = _to_dev_padded(z, v, dtype_name)
+    yt, yx = _to_dev_padded(y, v, dtype_name)
+    _say(f"widest rows {v} {dtype_name}: fused against separate calls")
+    off = torch.tensor([0, 2, n], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([2, 16], dtype=torch.int32, device="cuda")
+    out = lib.opd_fused_fwd_bwd_verify(zt, yt, off, lens, 0.6, 0.03, dz_dtype=torch.float32)
+    loss, a, d, stats = lib.opd_loss_fwd(zt, yt, 0.6, 0.03)
+    dz = lib.opd_loss_bwd(zt, yt, 0.6, 0.03, stats, a, dz_dtype=torch.float32)
+    a2, d2, acc = lib.verify_accept_len(zt, yt, off, lens)
+    torch.cuda.synchronize()
+    assert lib.read_flags(clear=True) == 0
+    assert torch.equal(loss, out["loss"])
+    assert torch.equal(stats, out["row_stats"])
+    assert torch.equal(a, out["target_top1"]) and torch.equal(d, out["draft_top1"])
+    assert torch.equal(a2, a) and torch.equal(d2, d)
+    assert torch.equal(acc, out["accept_len"])
+    assert torch.equal(dz, out["dz"])
+    assert np.array_equal(a.cpu().numpy(), O.top1_rows(yx))
+    assert np.array_equal(d.cpu().numpy(), O.top1_rows(zx))
+    dzn = out["dz"].cpu().numpy().astype(np.float64)
+    ln = out["loss"].cpu().numpy()
+    for r in (0, n - 1):
+        ok, msg = parity.check_row(zx[r], yx[r], 0.6, 0.03, ln[r], dzn[r])
+        assert ok, f"row {r}: {msg}"
+
+
 @pytest.mark.parametrize("dtype_name,v", [("bf16", 100003), ("f32", 77777), ("bf16", 151937), ("f32", 151937)])
 def test_batches_past_the_three_slot_plan(lib, dtype_name, v):
     """120 rows of a wide vocabulary: more rows than the three-slot plan has teams (at most about 90
